@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse prefill hot path on one MI355X.
+
+One step = the whole path for one layer over one batch of synthetic inputs
+already resident in HBM: pooling + block scores, selection, and block-sparse
+attention with mean correction.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+Workload (default): 64K-token bf16 GQA prefill, Hq=32, Hkv=8, d=128, B=128,
+alpha=0.05, sink 1 / window 2 / recent 1 blocks, mean correction on, inputs
+from the seeded planted-block generator (block-clustered keys; every query
+sums three visible block centres).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import (FP8_128K, GQA_BF16_16K, PAGED_VARLEN, SWEEP_BF16_64K,  # noqa: E402
+                       TINY_F32, make_inputs)
+
+METRIC = "sparse prefill ms/layer + dense-equiv TFLOP/s at 64K/128K (MFMA % of peak)"
+CONFIGS = {
+    "64k-bf16": SWEEP_BF16_64K,
+    "128k-fp8": FP8_128K,
+    "16k-bf16": GQA_BF16_16K,
+    "paged-varlen": PAGED_VARLEN,
+    "tiny-f32": TINY_F32,
+}
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def dense_flops(w) -> float:
+    """QK^T + PV over the causal triangle, every query head."""
+    return 4.0 * w.d * w.hq * sum(L * (L + 1) / 2 for L in w.seqlens)
+
+
+def effective_flops(w, cu: np.ndarray, idx: np.ndarray, correction: bool) -> tuple[float, float]:
+    """Attention FLOPs the selection asks for: visible (query, key) pairs of
+    the selected blocks (diagonal block counted causally) plus one pooled
+    term per corrected block, times 4*d.  Returns (flops, density)."""
+    pairs = 0.0
+    sel_total = 0
+    causal_total = 0
+    seg = 0
+    for L in w.seqlens:
+        N = -(-L // w.block)
+        for _h in range(w.hkv):
+            I = np.arange(N)
+            c = cu[seg + 1:seg + N + 1] - cu[seg:seg + N]
+            last = idx[cu[seg + 1:seg + N + 1] - 1]
+            diag = (c > 0) & (last == I)
+            nb = np.minimum(w.block, L - I * w.block).astype(np.float64)
+            off = (c - diag).astype(np.float64)
+            exact = nb * w.block * off + np.where(diag, nb * (nb + 1) / 2, 0.0)
+            todo = (I - off) if correction else np.zeros(N)
+            pairs += float(np.sum(w.g * (exact + nb * todo)))
+            sel_total += int(c.sum())
+            causal_total += N * (N + 1) // 2
+            seg += N
+    return 4.0 * w.d * pairs, sel_total / max(1, causal_total)
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle, as it stands, on the heaviest tiles of KV head 0,
+    until the time budget is spent; reported as dense-equivalent TFLOP/s of
+    the tiles it finished."""
+    import oracle
+    from oracle.fp8 import decode_e4m3fn
+
+    def deq(t, scale):
+        if w.dtype == "fp8":
+            return decode_e4m3fn(t.numpy()) * scale
+        return t.float().numpy().astype(np.float64)
+
+    L = w.seqlens[0]
+    N = -(-L // w.block)
+    h = 0
+    kk = inp.k_logical if inp.k_logical is not None else inp.k
+    vv = inp.v_logical if inp.v_logical is not None else inp.v
+    k = deq(kk[:L, h:h + 1].contiguous(), inp.k_scale)
+    v = deq(vv[:L, h:h + 1].contiguous(), inp.v_scale)
+    t0 = time.time()
+    kbar = oracle.pool_means(k, w.block)[:, 0]
+    vbar = oracle.pool_means(v, w.block)[:, 0]
+    t_pool = time.time() - t0
+    done = []
+    elapsed = t_pool
+    for I in range(N - 1, -1, -1):
+        nb = min(w.block, L - I * w.block)
+        # the tile's own rows, indexed from 0; positions shifted back afterwards
+        q_tile = deq(inp.q[I * w.block:I * w.block + nb].contiguous(), inp.q_scale)
+        t1 = time.time()
+        pos, heads, rows = oracle.tile_query_rows(q_tile, h, w.g, w.block, 0)
+        pos = pos + I * w.block
+        score = oracle.block_scores_row(rows, kbar, I, w.scale)
+        sel, _ = oracle.select_row(score, I, w.alpha, w.sink, w.window, w.recent)
+        todo = oracle.todo_row(sel, I, w.correction)
+        oracle.attend_rows(pos, rows, k[:, 0], v[:, 0], kbar, vbar, sel, todo, w.block, w.scale)
+        elapsed += time.time() - t1
+        done.append((I, nb))
+        if elapsed > budget_s and len(done) >= 2:
+            break
+    pairs = sum(w.g * (nb * I * w.block + nb * (nb + 1) / 2) for I, nb in done)
+    flops = 4.0 * w.d * pairs
+    threads = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        if info:
+            threads = max(int(x.get("num_threads", 1)) for x in info)
+    except Exception:  # noqa: BLE001
+        pass
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"numpy float64 oracle (pool + scores + select + attention) on KV head 0, "
+                   f"the {len(done)} heaviest query tiles I={done[-1][0]}..{done[0][0]} of "
+                   f"{N}, {elapsed:.1f} s wall"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="64k-bf16", choices=sorted(CONFIGS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the operator has no "
+              "cross-GPU step and this build runs on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_long_pooled_amd as bslp
+
+    w = CONFIGS[args.config]
+    t_gen = time.time()
+    inp = make_inputs(w, args.seed)
+    t_gen = time.time() - t_gen
+    dev = torch.device("cuda")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    table = torch.from_numpy(inp.table).to(dev) if inp.table is not None else None
+    prob = bslp.make_problem(w.dtype, w.hq, w.hkv, w.d, w.block, w.seqlens,
+                             softmax_scale=w.scale, q_scale=inp.q_scale, k_scale=inp.k_scale,
+                             v_scale=inp.v_scale, page_table=table, page_size=w.page_size)
+    params = bslp.make_params(w.alpha, w.sink, w.window, w.recent, w.correction)
+    bufs = bslp.Buffers(prob)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bslp.block_scores(prob, q, k, v, bufs.kbar, bufs.vbar, bufs.scores, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        bslp.select_blocks(prob, params, bufs.scores, bufs.counts, bufs.cu, bufs.idx, sp)
+        if ev is not None:
+            ev[2].record(stream)
+        bslp.sparse_prefill_attn(prob, params, q, k, v, bufs.kbar, bufs.vbar, bufs.cu, bufs.idx,
+                                 bufs.out, bufs.lse, sp)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                      for e in evs])
+    ms_step = wall * 1e3 / args.steps
+    ms_stage = stage.mean(axis=0)
+
+    cu = bufs.cu.cpu().numpy().astype(np.int64)
+    idx = bufs.idx.cpu().numpy().astype(np.int64)
+    f_eff, density = effective_flops(w, cu, idx, w.correction)
+    f_dense = dense_flops(w)
+    attn_ms = float(ms_stage[2])
+    achieved = f_eff / (attn_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+
+    # block-score stage algorithmic bytes: Q read once, K and V read once for
+    # pooling, pooled K/V written, score rows written
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
+    T = w.total_tokens
+    pooled = sum(-(-L // w.block) for L in w.seqlens)
+    score_elems = w.hkv * sum((-(-L // w.block)) * (-(-L // w.block) + 1) // 2 for L in w.seqlens)
+    s1_bytes = (T * w.hq * w.d * esz + 2 * T * w.hkv * w.d * esz + 2 * pooled * w.hkv * w.d * 4
+                + score_elems * 4)
+
+    res = {
+        "metric": METRIC,
+        "value": f_dense / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded planted-block generator)",
+        "config": {
+            "workload": w.name, "seqlens": list(w.seqlens), "hq": w.hq, "hkv": w.hkv,
+            "head_dim": w.d, "block": w.block, "alpha": w.alpha, "sink_blocks": w.sink,
+            "window_blocks": w.window, "recent_blocks": w.recent,
+            "mean_correction": bool(w.correction), "page_size": w.page_size,
+            "density": round(density, 5),
+        },
+        "ms_per_layer": ms_step,
+        "stages_ms": {"pool+block_scores": float(ms_stage[0]), "select_blocks": float(ms_stage[1]),
+                      "sparse_prefill_attn": attn_ms},
+        "roofline": {
+            "kernel": "sparse_prefill_attn",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": None,
+            "effective_flops": f_eff,
+        },
+        "block_scores_hbm": {"bytes": s1_bytes, "gbs": s1_bytes / (ms_stage[0] * 1e-3) / 1e9,
+                             "frac_of_8TBs": s1_bytes / (ms_stage[0] * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "input_gen_s": round(t_gen, 2),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

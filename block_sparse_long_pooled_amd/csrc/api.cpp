@@ -1,0 +1,207 @@
+// extern "C" entry points of libbslp: argument validation on the host, the
+// per-call plan (request table), then kernel launches on the caller's stream.
+// Nothing here allocates device memory, synchronises, or reads device memory.
+#include <cmath>
+#include <string>
+
+#include "bslp.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bslp_status fail(bslp_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
+
+bslp_status build_plan(const bslp_problem* pr, bslp::Plan* plan, bslp::KVDesc* kv) {
+  if (!pr) return fail(BSLP_ERR_INVALID_ARG, "problem is NULL");
+  if (pr->dtype < BSLP_F32 || pr->dtype > BSLP_FP8_E4M3)
+    return fail(BSLP_ERR_INVALID_ARG, "unknown dtype " + std::to_string(pr->dtype));
+  if (pr->num_heads_q < 1 || pr->num_heads_kv < 1)
+    return fail(BSLP_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (pr->num_heads_q % pr->num_heads_kv)
+    return fail(BSLP_ERR_INVALID_ARG, "num_heads_q must be a multiple of num_heads_kv");
+  const int g = pr->num_heads_q / pr->num_heads_kv;
+  if (g > bslp::kMaxGroup)
+    return fail(BSLP_ERR_UNSUPPORTED, "group size Hq/Hkv above 16 is not built");
+  if (pr->head_dim != 64 && pr->head_dim != 128)
+    return fail(BSLP_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (pr->block_size != 64 && pr->block_size != 128)
+    return fail(BSLP_ERR_UNSUPPORTED, "block_size must be 64 or 128");
+  if (!finite_pos(pr->softmax_scale))
+    return fail(BSLP_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (!finite_pos(pr->q_scale) || !finite_pos(pr->k_scale) || !finite_pos(pr->v_scale))
+    return fail(BSLP_ERR_INVALID_ARG, "q/k/v scales must be finite and > 0");
+  if (pr->dtype != BSLP_FP8_E4M3 &&
+      (pr->q_scale != 1.f || pr->k_scale != 1.f || pr->v_scale != 1.f))
+    return fail(BSLP_ERR_INVALID_ARG, "q/k/v scales must be 1 unless dtype is fp8");
+  if (pr->num_seqs < 1) return fail(BSLP_ERR_INVALID_ARG, "num_seqs must be >= 1");
+  if (pr->num_seqs > bslp::kMaxSeqs)
+    return fail(BSLP_ERR_UNSUPPORTED, "more than 64 packed requests per call");
+  if (!pr->seqlens) return fail(BSLP_ERR_INVALID_ARG, "seqlens is NULL");
+  int page_shift = 0;
+  if (pr->page_table) {
+    const int ps = pr->page_size;
+    if (ps < 1 || ps > (1 << 20) || (ps & (ps - 1)))
+      return fail(BSLP_ERR_INVALID_ARG, "page_size must be a power of two in [1, 2^20]");
+    while ((1 << page_shift) < ps) ++page_shift;
+    if (pr->max_pages_per_seq < 1)
+      return fail(BSLP_ERR_INVALID_ARG, "max_pages_per_seq must be >= 1");
+  }
+
+  *plan = bslp::Plan{};
+  plan->num_seqs = pr->num_seqs;
+  plan->hq = pr->num_heads_q;
+  plan->hkv = pr->num_heads_kv;
+  plan->g = g;
+  plan->d = pr->head_dim;
+  plan->B = pr->block_size;
+  int64_t tok = 0, pool = 0, seg = 0, score = 0;
+  int max_nblk = 0;
+  for (int b = 0; b < pr->num_seqs; ++b) {
+    const int64_t L = pr->seqlens[b];
+    if (L < 0) return fail(BSLP_ERR_INVALID_ARG, "negative sequence length");
+    const int64_t N = (L + plan->B - 1) / plan->B;
+    if (N > bslp::kMaxBlocksPerSeq)
+      return fail(BSLP_ERR_UNSUPPORTED, "more than 16384 blocks in one request");
+    if (pr->page_table && (L + pr->page_size - 1) / pr->page_size > pr->max_pages_per_seq)
+      return fail(BSLP_ERR_INVALID_ARG, "request longer than max_pages_per_seq pages");
+    bslp::SeqInfo& s = plan->seq[b];
+    s.tok_start = (int32_t)tok;
+    s.len = (int32_t)L;
+    s.nblk = (int32_t)N;
+    s.pool_base = (int32_t)pool;
+    s.seg_base = (int32_t)seg;
+    s.unit_base = 0;
+    s.score_base = score;
+    tok += L;
+    pool += N;
+    seg += (int64_t)plan->hkv * N;
+    score += (int64_t)plan->hkv * N * (N + 1) / 2;
+    if (N > max_nblk) max_nblk = (int)N;
+    if (tok >= (int64_t(1) << 31) || score >= (int64_t(1) << 31))
+      return fail(BSLP_ERR_UNSUPPORTED, "problem exceeds 2^31 tokens or index entries");
+  }
+  plan->max_nblk = max_nblk;
+  plan->total_tokens = tok;
+  plan->pooled_rows = pool;
+  plan->num_segments = seg;
+  plan->score_elems = score;
+  kv->page_table = pr->page_table;
+  kv->page_shift = page_shift;
+  kv->max_pages = pr->page_table ? pr->max_pages_per_seq : 0;
+  return BSLP_OK;
+}
+
+bslp_status check_params(const bslp_select_params* a, bslp::SelectArgs* out) {
+  if (!a) return fail(BSLP_ERR_INVALID_ARG, "params is NULL");
+  if (!std::isfinite(a->alpha) || a->alpha < 0.f)
+    return fail(BSLP_ERR_INVALID_ARG, "alpha must be finite and >= 0");
+  if (a->sink_blocks < 0 || a->window_blocks < 0 || a->recent_blocks < 0)
+    return fail(BSLP_ERR_INVALID_ARG, "sink/window/recent block counts must be >= 0");
+  if (a->mean_correction != 0 && a->mean_correction != 1)
+    return fail(BSLP_ERR_INVALID_ARG, "mean_correction must be 0 or 1");
+  out->alpha = a->alpha;
+  out->sink = a->sink_blocks;
+  out->window = a->window_blocks;
+  out->recent = a->recent_blocks;
+  out->correction = a->mean_correction;
+  return BSLP_OK;
+}
+
+bslp_status hip_result(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BSLP_OK;
+  return fail(BSLP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+bslp_status bslp_get_sizes(const bslp_problem* problem, bslp_sizes* out) {
+  bslp::Plan plan;
+  bslp::KVDesc kv;
+  if (!out) return fail(BSLP_ERR_INVALID_ARG, "sizes output is NULL");
+  const bslp_status st = build_plan(problem, &plan, &kv);
+  if (st != BSLP_OK) return st;
+  out->total_tokens = plan.total_tokens;
+  out->pooled_rows = plan.pooled_rows;
+  out->score_elems = plan.score_elems;
+  out->num_segments = plan.num_segments;
+  return BSLP_OK;
+}
+
+bslp_status bslp_block_scores(const bslp_problem* problem, const void* q, const void* k,
+                              const void* v, float* kbar, float* vbar, float* scores,
+                              void* stream) {
+  bslp::Plan plan;
+  bslp::KVDesc kv;
+  bslp_status st = build_plan(problem, &plan, &kv);
+  if (st != BSLP_OK) return st;
+  if (plan.total_tokens == 0) return BSLP_OK;
+  if (!q || !k || !v || !kbar || !vbar || !scores)
+    return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  return hip_result(bslp::launch_stage1(plan, kv, problem->dtype, q, k, v, problem->q_scale,
+                                        problem->k_scale, problem->v_scale,
+                                        problem->softmax_scale, kbar, vbar, scores,
+                                        (hipStream_t)stream),
+                    "bslp_block_scores");
+}
+
+bslp_status bslp_select_blocks(const bslp_problem* problem, const bslp_select_params* params,
+                               const float* scores, int32_t* counts, int32_t* cu, int32_t* idx,
+                               void* stream) {
+  bslp::Plan plan;
+  bslp::KVDesc kv;
+  bslp::SelectArgs a;
+  bslp_status st = build_plan(problem, &plan, &kv);
+  if (st != BSLP_OK) return st;
+  st = check_params(params, &a);
+  if (st != BSLP_OK) return st;
+  if (!cu) return fail(BSLP_ERR_INVALID_ARG, "cu is NULL");
+  if (plan.num_segments > 0 && (!scores || !counts || !idx))
+    return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  return hip_result(bslp::launch_select(plan, a, scores, counts, cu, idx, (hipStream_t)stream),
+                    "bslp_select_blocks");
+}
+
+bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
+                                     const bslp_select_params* params, const void* q,
+                                     const void* k, const void* v, const float* kbar,
+                                     const float* vbar, const int32_t* cu, const int32_t* idx,
+                                     void* out, float* lse, void* stream) {
+  bslp::Plan plan;
+  bslp::KVDesc kv;
+  bslp::SelectArgs sa;
+  bslp_status st = build_plan(problem, &plan, &kv);
+  if (st != BSLP_OK) return st;
+  st = check_params(params, &sa);
+  if (st != BSLP_OK) return st;
+  if (plan.total_tokens == 0) return BSLP_OK;
+  if (!q || !k || !v || !kbar || !vbar || !cu || !idx || !out)
+    return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  bslp::AttnArgs a{q, k, v, kbar, vbar, cu, idx, out, lse,
+                   problem->softmax_scale * problem->q_scale, problem->k_scale,
+                   problem->v_scale, sa.correction};
+  return hip_result(bslp::launch_attn_valu(plan, kv, problem->dtype, a, (hipStream_t)stream),
+                    "bslp_sparse_prefill_attn");
+}
+
+const char* bslp_status_string(bslp_status status) {
+  switch (status) {
+    case BSLP_OK: return "ok";
+    case BSLP_ERR_INVALID_ARG: return "invalid argument";
+    case BSLP_ERR_UNSUPPORTED: return "unsupported";
+    case BSLP_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* bslp_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

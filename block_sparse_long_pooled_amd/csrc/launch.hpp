@@ -1,0 +1,36 @@
+// Internal launchers of libbslp (host side).  Each enqueues its kernels on the
+// given stream and returns the first HIP error, if any.
+#pragma once
+
+#include "common.hpp"
+
+namespace bslp {
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* kbar;
+  const float* vbar;
+  const int32_t* cu;
+  const int32_t* idx;
+  void* out;
+  float* lse;
+  float lscale;   // softmax_scale * q_scale
+  float k_scale;  // 1 unless fp8
+  float v_scale;
+  int correction;
+};
+
+hipError_t launch_stage1(const Plan& p, const KVDesc& kv, int dtype, const void* q, const void* k,
+                         const void* v, float q_scale, float k_scale, float v_scale,
+                         float softmax_scale, float* kbar, float* vbar, float* scores,
+                         hipStream_t st);
+
+hipError_t launch_select(const Plan& p, const SelectArgs& a, const float* scores, int32_t* counts,
+                         int32_t* cu, int32_t* idx, hipStream_t st);
+
+hipError_t launch_attn_valu(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
+                            hipStream_t st);
+
+}  // namespace bslp

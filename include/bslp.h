@@ -1,0 +1,177 @@
+/*
+ * bslp.h - C ABI of libbslp, an MI355X (gfx950) block-sparse prefill
+ * attention library implementing the FlashPrefill / FlashPrefill V2 hot path:
+ *
+ *   1. bslp_block_scores   mean-pooled keys/values and fused block scores
+ *   2. bslp_select_blocks  max-based threshold + sink/window/recent blocks,
+ *                          emitted as a CSR selected-block index
+ *   3. bslp_sparse_prefill_attn
+ *                          causal block-sparse online-softmax attention over
+ *                          the selected blocks, with mean correction for the
+ *                          pruned fully-visible blocks and PackGQA rows
+ *
+ * Sources (page title, section):
+ *   "FlashPrefill V2: Block-Sparse Prefill Attention for Long-Context LLM
+ *   Serving", Sec. 3.1, Sec. 3.2, the PackGQA, FP8, CSR, paged-KV and
+ *   integration paragraphs; "FlashPrefill: Instantaneous Pattern Discovery
+ *   and Thresholding for Ultra-Fast Long-Context Prefilling" (summary page),
+ *   method-steps section.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership: the caller allocates and owns every buffer.  The library never
+ *   allocates, frees or keeps a pointer after a call returns.  Device pointers
+ *   must stay valid until the work enqueued on `stream` has finished.
+ * Streams: `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *   enqueued on it; no call synchronises the host or reads device memory back.
+ * Errors: every argument is validated on the host before anything is
+ *   launched; a call that returns an error has enqueued nothing.  Launch
+ *   failures return BSLP_ERR_HIP.  bslp_last_error() gives a thread-local text
+ *   for the last failing call of the calling thread.  No exception crosses
+ *   the ABI and there is no global mutable state besides that text.
+ * Sequences: requests are packed back to back ("varlen"); request b owns
+ *   token rows [start_b, start_b + L_b) with start_b = L_0 + ... + L_{b-1};
+ *   queries and keys share positions (self prefill, L_q = L_kv).
+ * Blocks: key block J of request b covers tokens [J*B, min((J+1)*B, L_b));
+ *   N_b = ceil(L_b / B).  Query tile I covers the same positions for the g =
+ *   Hq/Hkv query heads of one KV head (PackGQA rows, FlashPrefill V2 PackGQA
+ *   paragraph); one selection is made per (request, KV head, tile).
+ * Segments: s(b, h, I) = seg_base_b + h*N_b + I with seg_base_b =
+ *   sum_{b'<b} Hkv*N_b'.  Score rows: row (b, h, I) has I+1 floats at
+ *   score_base_b + h*N_b(N_b+1)/2 + I(I+1)/2, score_base_b = sum_{b'<b}
+ *   Hkv*N_b'(N_b'+1)/2.  Pooled rows: block J of request b is pooled row
+ *   pool_base_b + J, pool_base_b = sum_{b'<b} N_b'.
+ */
+#ifndef BSLP_H
+#define BSLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bslp_status {
+  BSLP_OK = 0,
+  BSLP_ERR_INVALID_ARG = 1, /* null pointer, inconsistent shape, bad value  */
+  BSLP_ERR_UNSUPPORTED = 2, /* valid but not built (head_dim, block, limits) */
+  BSLP_ERR_HIP = 3          /* a HIP launch or runtime call failed          */
+} bslp_status;
+
+typedef enum bslp_dtype {
+  BSLP_F32 = 0,      /* float32 Q/K/V, float32 output                       */
+  BSLP_BF16 = 1,     /* bfloat16 Q/K/V, bfloat16 output                     */
+  BSLP_FP8_E4M3 = 2  /* OCP e4m3fn codes (uint8) with one float scale per
+                        tensor (FlashPrefill V2, FP8 paragraph); bf16 output */
+} bslp_dtype;
+
+/* Problem descriptor; read during the call only. */
+typedef struct bslp_problem {
+  int32_t dtype;          /* bslp_dtype                                      */
+  int32_t num_heads_q;    /* Hq                                              */
+  int32_t num_heads_kv;   /* Hkv; Hq % Hkv == 0, g = Hq / Hkv <= 16          */
+  int32_t head_dim;       /* d: 64 or 128                                    */
+  int32_t block_size;     /* B: 64 or 128                                    */
+  float softmax_scale;    /* multiplies q.k (normally 1/sqrt(d)), > 0        */
+  float q_scale;          /* per-tensor dequantisation scales for fp8; each  */
+  float k_scale;          /*   fp8 element x decodes to code(x) * scale.     */
+  float v_scale;          /*   Must be 1 for f32 / bf16.                     */
+  int32_t num_seqs;       /* 1 .. 64                                         */
+  const int32_t* seqlens; /* HOST array [num_seqs], each L_b >= 0, N_b <= 16384 */
+  /* Paged K/V (FlashPrefill V2, paged-KV paragraph): when page_table is not
+   * NULL, key/value token j of request b lives at physical row
+   * page_table[b * max_pages_per_seq + j / page_size] * page_size
+   * + j % page_size of the K/V arrays.  page_size is a power of two.
+   * Entries must address rows inside the caller's K/V arrays; they are not
+   * range-checked on the device. */
+  const int32_t* page_table; /* DEVICE [num_seqs, max_pages_per_seq] or NULL */
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+} bslp_problem;
+
+/* Selection hyper-parameters (FlashPrefill V2, Sec. 3.1 and Sec. 4: alpha and
+ * the sink/window sizes are user settings).  Counts are in blocks:
+ *   sink   = blocks 0 .. sink_blocks-1,
+ *   recent = the recent_blocks blocks ending at the diagonal block I,
+ *   window = the window_blocks blocks just before the recent ones,
+ * all clipped to 0 .. I. */
+typedef struct bslp_select_params {
+  float alpha;             /* thresh_I = alpha * max_J Score_IJ, alpha >= 0  */
+  int32_t sink_blocks;     /* >= 0 */
+  int32_t window_blocks;   /* >= 0 */
+  int32_t recent_blocks;   /* >= 0 */
+  int32_t mean_correction; /* 0 or 1 */
+} bslp_select_params;
+
+/* Buffer sizes implied by a problem. */
+typedef struct bslp_sizes {
+  int64_t total_tokens; /* T = sum L_b: rows of Q, O and (contiguous) K/V     */
+  int64_t pooled_rows;  /* sum N_b: rows of kbar / vbar                       */
+  int64_t score_elems;  /* sum Hkv N_b (N_b+1)/2: scores and idx capacity     */
+  int64_t num_segments; /* sum Hkv N_b: entries of counts (cu has one more)   */
+} bslp_sizes;
+
+/* Validates `problem` and fills `out`.  Host only; no HIP call. */
+bslp_status bslp_get_sizes(const bslp_problem* problem, bslp_sizes* out);
+
+/* Stage 1: pooled means and block scores.
+ *
+ * Pooling (FlashPrefill V2, Sec. 3.1; pooled values for Sec. 3.2):
+ *   kbar[pool_base_b + J, h, :] = mean of k over the tokens of block J,
+ *   vbar likewise; float32 [pooled_rows, Hkv, d].  For fp8 the means are of
+ *   the dequantised values (code * k_scale).
+ * Scores (FlashPrefill summary page, method steps; V2 Sec. 3.1): for every
+ *   (b, h, I) and J <= I, with s_rJ = softmax_scale * q_r . kbar_J over the
+ *   tile's g*|tile| rows r (block-causal, no token mask in the diagonal
+ *   block), M_I = max_{r, J<=I} s_rJ, S'_IJ = sum_r exp(s_rJ - M_I),
+ *   Score_IJ = S'_IJ / sum_{K<=I} S'_IK, written to scores (float32 rows as
+ *   described above).  Logits are accumulated in float64.
+ *
+ * q: [T, Hq, d] in the problem dtype.  k, v: [T, Hkv, d], or physical rows
+ * [*, Hkv, d] through the page table.  All device pointers. */
+bslp_status bslp_block_scores(const bslp_problem* problem, const void* q, const void* k,
+                              const void* v, float* kbar, float* vbar, float* scores,
+                              void* stream);
+
+/* Stage 2: selection (FlashPrefill V2, Sec. 3.1 threshold paragraph and the
+ * CSR paragraph; threshold formula printed on the FlashPrefill summary page).
+ *   thresh_I = alpha * max_{J<=I} Score_IJ;
+ *   Sel_I = {J <= I : Score_IJ >= thresh_I} u sink u window u recent.
+ * Outputs (device, int32):
+ *   counts[s] = |Sel| of segment s                        [num_segments]
+ *   cu[s]     = sum_{s'<s} counts[s'], cu[num_segments] = total
+ *                                                         [num_segments + 1]
+ *   idx[cu[s] .. cu[s+1]) = Sel of segment s, ascending  [score_elems capacity]
+ * alpha = 0 selects every causal block (dense attention). */
+bslp_status bslp_select_blocks(const bslp_problem* problem, const bslp_select_params* params,
+                               const float* scores, int32_t* counts, int32_t* cu, int32_t* idx,
+                               void* stream);
+
+/* Stage 3: block-sparse causal attention with mean correction
+ * (FlashPrefill V2, Sec. 3.1 last sentence, Sec. 3.2 and Fig. 3, PackGQA and
+ * CSR paragraphs).  For query row (i, hq) of tile I, KV head h = hq / g:
+ *   exact terms  e_j = softmax_scale * q . k_j for the tokens j <= i of the
+ *                blocks in Sel_I (read from cu/idx);
+ *   correction   if params->mean_correction: for every J <= I-1 not in Sel_I,
+ *                c_J = softmax_scale * q . kbar_J + ln|B_J| with value vbar_J;
+ *   O = sum softmax weights * values, LSE = m + ln l (natural log).
+ * out: [T, Hq, d], float32 for BSLP_F32 else bfloat16.  lse: float32
+ * [Hq, T] or NULL.  A row that sees no key gets O = 0 and LSE = -inf.
+ * kbar / vbar / cu / idx are the outputs of stages 1 and 2 for the same
+ * problem.  Only params->mean_correction is read. */
+bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
+                                     const bslp_select_params* params, const void* q,
+                                     const void* k, const void* v, const float* kbar,
+                                     const float* vbar, const int32_t* cu, const int32_t* idx,
+                                     void* out, float* lse, void* stream);
+
+/* Static text for a status code. */
+const char* bslp_status_string(bslp_status status);
+/* Detail of the calling thread's last failing call ("" if none). */
+const char* bslp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSLP_H */

@@ -1,0 +1,139 @@
+"""The C-ABI library loads on a machine without a GPU, exports every entry
+point the header declares, and rejects bad arguments on the host before any
+HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_long_pooled_amd as bslp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bslp.LIB_PATH),
+                                reason="libbslp.so not built")
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "bslp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bslp_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = bslp.load_library()
+    names = header_functions()
+    assert set(names) == set(bslp.EXPORTS)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def _problem(**kw):
+    args = dict(dtype="bf16", hq=8, hkv=2, head_dim=128, block_size=128, seqlens=[1000, 300])
+    args.update(kw)
+    return bslp.make_problem(**args)
+
+
+def test_sizes_match_the_layout():
+    p = _problem()
+    s = bslp.get_sizes(p)
+    N = [8, 3]
+    assert s.total_tokens == 1300
+    assert s.pooled_rows == sum(N)
+    assert s.num_segments == 2 * sum(N)
+    assert s.score_elems == 2 * sum(n * (n + 1) // 2 for n in N)
+
+
+def _status(fn):
+    with pytest.raises(bslp.BslpError) as e:
+        fn()
+    return e.value.status, e.value.detail
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), 1),
+    (dict(hq=6, hkv=4), 1),
+    (dict(hq=0), 1),
+    (dict(hq=34, hkv=2), 2),
+    (dict(head_dim=96), 2),
+    (dict(block_size=32), 2),
+    (dict(softmax_scale=float("nan")), 1),
+    (dict(softmax_scale=-1.0), 1),
+    (dict(q_scale=2.0), 1),
+    (dict(dtype="fp8", k_scale=0.0), 1),
+    (dict(seqlens=[]), 1),
+    (dict(seqlens=[5] * 65), 2),
+    (dict(seqlens=[10, -1]), 1),
+    (dict(seqlens=[128 * 16385]), 2),
+])
+def test_problem_validation(kw, status):
+    st, detail = _status(lambda: bslp.get_sizes(_problem(**kw)))
+    assert st == status and detail
+
+
+class FakeTensor:
+    """Stands in for a device tensor: a pointer that is never dereferenced."""
+
+    def __init__(self, shape=(4, 4)):
+        self.shape = shape
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return 0x1000
+
+
+def test_page_table_validation():
+    pt = FakeTensor((2, 4))
+    st, _ = _status(lambda: bslp.get_sizes(_problem(page_table=pt, page_size=96)))
+    assert st == 1
+    st, _ = _status(lambda: bslp.get_sizes(_problem(page_table=pt, page_size=64)))
+    assert st == 1  # 1000 tokens need 16 pages of 64 > 4
+    assert bslp.get_sizes(_problem(page_table=pt, page_size=256)).total_tokens == 1300
+
+
+@pytest.mark.parametrize("kw", [dict(alpha=-0.1), dict(alpha=float("inf")), dict(sink=-1),
+                                dict(correction=2)])
+def test_params_validation(kw):
+    args = dict(alpha=0.05, sink=1, window=2, recent=1, correction=True)
+    args.update(kw)
+    params = bslp.make_params(**args)
+    if kw.get("correction") == 2:
+        params.mean_correction = 2
+    t = FakeTensor()
+    st, _ = _status(lambda: bslp.select_blocks(_problem(), params, t, t, t, t, stream=0))
+    assert st == 1
+
+
+def test_null_pointers_rejected_before_launch():
+    p = _problem()
+    params = bslp.make_params(0.05)
+    t = FakeTensor()
+    st, d = _status(lambda: bslp.block_scores(p, t, t, None, t, t, t, stream=0))
+    assert st == 1 and "NULL" in d
+    st, _ = _status(lambda: bslp.select_blocks(p, params, t, t, None, t, stream=0))
+    assert st == 1
+    st, _ = _status(lambda: bslp.sparse_prefill_attn(p, params, t, t, t, t, t, t, None, t,
+                                                     stream=0))
+    assert st == 1
+    st, _ = _status(lambda: bslp.sparse_prefill_attn(None or _problem(head_dim=80), params,
+                                                     t, t, t, t, t, t, t, t, stream=0))
+    assert st == 2
+
+
+def test_empty_problem_enqueues_nothing():
+    p = _problem(seqlens=[0, 0])
+    s = bslp.get_sizes(p)
+    assert s.total_tokens == 0 and s.num_segments == 0
+    bslp.block_scores(p, None, None, None, None, None, None, stream=0)
+    bslp.sparse_prefill_attn(p, bslp.make_params(0.1), None, None, None, None, None, None,
+                             None, None, stream=0)
+
+
+def test_status_strings():
+    lib = bslp.load_library()
+    assert lib.bslp_status_string(0) == b"ok"
+    assert lib.bslp_status_string(2) == b"unsupported"
+    assert isinstance(lib.bslp_last_error(), bytes)
