@@ -188,8 +188,13 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
   bslp::AttnArgs a{q, k, v, kbar, vbar, cu, idx, out, lse,
                    problem->softmax_scale * problem->q_scale, problem->k_scale,
                    problem->v_scale, sa.correction};
-  return hip_result(bslp::launch_attn_valu(plan, kv, problem->dtype, a, (hipStream_t)stream),
-                    "bslp_sparse_prefill_attn");
+  // bf16 runs on the matrix cores; float32 keeps exact fp32 arithmetic on the
+  // vector ALUs.
+  const hipError_t e = problem->dtype == BSLP_BF16
+                           ? bslp::launch_attn_mfma_bf16(plan, kv, a, (hipStream_t)stream)
+                           : bslp::launch_attn_valu(plan, kv, problem->dtype, a,
+                                                    (hipStream_t)stream);
+  return hip_result(e, "bslp_sparse_prefill_attn");
 }
 
 const char* bslp_status_string(bslp_status status) {

@@ -33,4 +33,7 @@ hipError_t launch_select(const Plan& p, const SelectArgs& a, const float* scores
 hipError_t launch_attn_valu(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
                             hipStream_t st);
 
+hipError_t launch_attn_mfma_bf16(const Plan& p, const KVDesc& kv, const AttnArgs& a,
+                                 hipStream_t st);
+
 }  // namespace bslp
