@@ -27,6 +27,12 @@ hipError_t launch_stage1(const Plan& p, const KVDesc& kv, int dtype, const void*
                          float softmax_scale, float* kbar, float* vbar, float* scores,
                          hipStream_t st);
 
+// Block scores on the matrix cores (bf16 / fp8 inputs, g*B <= 1024 rows per
+// tile); c2 = softmax_scale * q_scale * log2(e).
+bool scores_mfma_supported(const Plan& p, int dtype);
+hipError_t launch_scores_mfma(const Plan& p, int dtype, const void* q, const float* kbar,
+                              float c2, float* scores, hipStream_t st);
+
 hipError_t launch_select(const Plan& p, const SelectArgs& a, const float* scores, int32_t* counts,
                          int32_t* cu, int32_t* idx, hipStream_t st);
 

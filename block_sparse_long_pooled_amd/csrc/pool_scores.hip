@@ -192,6 +192,10 @@ static hipError_t launch_stage1_t(const Plan& p, const KVDesc& kv, const void* q
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (p.num_segments > 0 && scores_mfma_supported(p, DT)) {
+    const double c2 = (double)softmax_scale * (double)q_scale * 1.4426950408889634;
+    return launch_scores_mfma(p, DT, q, kbar, (float)c2, scores, st);
+  }
   if (p.num_segments > 0) {
     const int nch = (p.max_nblk + 31) / 32;
     const size_t lds = sizeof(double) * (2 * nch);

@@ -1,0 +1,319 @@
+// Stage 1 block scores on the matrix cores (bf16 and fp8 inputs).
+//
+// Computes, for every segment (b, h, I), the FlashPrefill block scores over
+// the mean-pooled keys ("FlashPrefill V2", Sec. 3.1 and the paragraph that
+// fuses scoring and thresholding; formulas printed in the method-steps
+// section of the FlashPrefill summary page):
+//   s_rJ     = softmax_scale * q_r . kbar_J        (r: the g*|tile| PackGQA rows)
+//   M_I      = max_{r, J<=I} s_rJ
+//   Score_IJ = sum_r exp(s_rJ - M_I) / sum_{K<=I} sum_r exp(s_rK - M_I)
+//
+// Accuracy.  The selection that follows must agree with a float64 evaluation
+// except within 1e-5 (relative) of the threshold, so the logits need about
+// 1e-6 absolute accuracy.  q is exact in bf16 (bf16 input, or an e4m3 code,
+// whose 4 significant bits fit).  kbar (float32) is split exactly into three
+// bf16 terms, kbar = hi + mid + lo (truncation leaves 8 significant bits per
+// term), every bf16 x bf16 product is exact in float32, and the MFMA sums
+// are accumulated lo first, then mid, then hi, so only the last eight
+// accumulations run at the magnitude of the logit.
+//
+// Work layout.  One workgroup per segment, NW waves; wave w owns RT row tiles
+// of 32 packed rows (Q in registers as the A operand of
+// v_mfma_f32_32x32x16_bf16).  Key blocks are processed in chunks of 32: the
+// chunk's split kbar rows are staged in LDS (double buffered, next chunk
+// prefetched into registers while the current one is multiplied) and read
+// as the B operand, so in the 32x32 accumulator every lane owns one key
+// block J (its column) and 16 rows.  Each lane reduces its rows in-lane
+// (max, then sum of exp2), the two lane halves combine with
+// v_permlane32_swap, the waves combine through LDS, and one wave turns the
+// chunk into E_J = S_J * 2^(m_J - M_c) with the chunk maximum M_c (the
+// per-chunk maximum of the V2 index buffer).  A final pass rescales E_J by
+// 2^(M_c - M_I) and divides by the row total.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace bslp {
+
+typedef __bf16 sbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float sf32x16_t __attribute__((ext_vector_type(16)));
+
+namespace {
+
+constexpr int kChunk = 32;  // key blocks per chunk = MFMA N
+
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Exact three-term split of a float into bf16 bit patterns (x = hi + mid + lo).
+__device__ __forceinline__ void split3(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  const uint32_t xb = __float_as_uint(x);
+  const uint32_t hb = xb & 0xffff0000u;
+  const float r1 = x - __uint_as_float(hb);
+  const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+  const float r2 = r1 - __uint_as_float(mb);
+  hi = (uint16_t)(hb >> 16);
+  mid = (uint16_t)(mb >> 16);
+  lo = (uint16_t)(__float_as_uint(r2) >> 16);
+}
+
+// 8 consecutive query elements as bf16 (exact for bf16 and e4m3 inputs).
+template <int DT>
+__device__ __forceinline__ uint4 load_q8_bf16(const typename Elem<DT>::T* p, int64_t off) {
+  if constexpr (DT == kBF16) {
+    return *reinterpret_cast<const uint4*>(p + off);
+  } else {
+    const uint2 u = *reinterpret_cast<const uint2*>(p + off);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t word = i < 2 ? u.x : u.y;
+      const int sh = 16 * (i & 1);
+      const uint32_t a = __float_as_uint(e4m3_to_f32((uint8_t)(word >> sh))) >> 16;
+      const uint32_t b = __float_as_uint(e4m3_to_f32((uint8_t)(word >> (sh + 8)))) >> 16;
+      w[i] = a | (b << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+}  // namespace
+
+template <int DT, int D, int RT, int NW>
+__global__ __launch_bounds__(NW * 64) void scores_mfma_kernel(Plan p,
+                                                              const typename Elem<DT>::T* __restrict__ q,
+                                                              const float* __restrict__ kbar,
+                                                              float c2, float* __restrict__ scores) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = D / 16;            // k-steps of 16 dims
+  constexpr int LD = D + 8;             // padded LDS row (bf16), 16-byte multiple
+  constexpr int F4 = kChunk * D / 4;    // float4 per kbar chunk
+  constexpr int PF = (F4 + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) uint16_t kb[2][3][kChunk * LD];
+  __shared__ float part_m[2][NW][kChunk];
+  __shared__ float part_s[2][NW][kChunk];
+  __shared__ float fin[2];
+  extern __shared__ float dyn[];  // cmax[nch], csum[nch]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int jj = lane & 31;
+  const int64_t seg = p.num_segments - 1 - (int64_t)blockIdx.x;  // longest rows first
+  const int b = seq_of_segment(p, seg);
+  const SeqInfo s = p.seq[b];
+  const int local = (int)(seg - s.seg_base);
+  const int h = local / s.nblk;
+  const int I = local % s.nblk;
+  const int nb = min(p.B, s.len - I * p.B);
+  const int R = p.g * nb;
+  const int nJ = I + 1;
+  const int nch = (nJ + kChunk - 1) / kChunk;
+  float* cmax = dyn;
+  float* csum = dyn + nch;
+  float* row_out = scores + score_offset(s, h, I);
+  const float* kb_head = kbar + ((int64_t)s.pool_base * p.hkv + h) * D;
+  const int64_t kb_stride = (int64_t)p.hkv * D;  // floats between pooled rows
+
+  // ---- this wave's query rows (A operands), zero beyond R
+  const int row0 = wave * RT * 32;
+  const bool wave_active = row0 < R;
+  sbf16x8_t qa[RT][KS];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int r = row0 + t * 32 + jj;
+    const bool ok = r < R;
+    const int pos = I * p.B + (ok ? r / p.g : 0);
+    const int hq = h * p.g + (ok ? r % p.g : 0);
+    const int64_t qoff = ((int64_t)(s.tok_start + pos) * p.hq + hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (ok) u = load_q8_bf16<DT>(q, qoff + ks * 16 + half * 8);
+      qa[t][ks] = __builtin_bit_cast(sbf16x8_t, u);
+    }
+  }
+
+  // ---- kbar chunk staging: global float32 -> registers -> split bf16 in LDS
+  float4 pf[PF];
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int f = tid + i * NT;
+      const int j = f / (D / 4);
+      const int J = c * kChunk + j;
+      pf[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if ((F4 % NT == 0 || f < F4) && J < nJ)
+        pf[i] = *reinterpret_cast<const float4*>(kb_head + (int64_t)J * kb_stride +
+                                                 (f % (D / 4)) * 4);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int f = tid + i * NT;
+      if (F4 % NT != 0 && f >= F4) break;
+      const int j = f / (D / 4);
+      const int d0 = (f % (D / 4)) * 4;
+      const float xv[4] = {pf[i].x, pf[i].y, pf[i].z, pf[i].w};
+      uint16_t hs[4], ms[4], ls[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split3(xv[e], hs[e], ms[e], ls[e]);
+      const int o = j * LD + d0;
+      *reinterpret_cast<uint2*>(&kb[buf][0][o]) =
+          make_uint2(hs[0] | ((uint32_t)hs[1] << 16), hs[2] | ((uint32_t)hs[3] << 16));
+      *reinterpret_cast<uint2*>(&kb[buf][1][o]) =
+          make_uint2(ms[0] | ((uint32_t)ms[1] << 16), ms[2] | ((uint32_t)ms[3] << 16));
+      *reinterpret_cast<uint2*>(&kb[buf][2][o]) =
+          make_uint2(ls[0] | ((uint32_t)ls[1] << 16), ls[2] | ((uint32_t)ls[3] << 16));
+    }
+  };
+
+  fetch(0);
+  store(0);
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) fetch(c + 1);
+    float pm = -INFINITY, ps = 0.f;
+    if (wave_active) {
+      sf32x16_t acc[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+      }
+      // lo, mid, hi: small partial sums first
+#pragma unroll
+      for (int sp = 2; sp >= 0; --sp) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const sbf16x8_t bop = *reinterpret_cast<const sbf16x8_t*>(
+              &kb[buf][sp][jj * LD + ks * 16 + half * 8]);
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t][ks], bop, acc[t], 0, 0, 0);
+        }
+      }
+      const int J = c * kChunk + jj;
+      const bool okJ = J < nJ;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = row0 + t * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+          const float x = (okJ && r < R) ? acc[t][i] * c2 : -INFINITY;
+          acc[t][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = pair_max(mx);
+      const float mu = mx == -INFINITY ? 0.f : mx;
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(acc[t][i] - mu);
+      }
+      pm = mx;
+      ps = pair_sum(sum);
+    }
+    if (half == 0) {
+      part_m[buf][wave][jj] = pm;
+      part_s[buf][wave][jj] = ps;
+    }
+    if (c + 1 < nch) store(buf ^ 1);
+    __syncthreads();
+    if (wave == 0 && half == 0) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) m = fmaxf(m, part_m[buf][w][jj]);
+      const float mu = m == -INFINITY ? 0.f : m;
+      float S = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) S += part_s[buf][w][jj] * __builtin_amdgcn_exp2f(part_m[buf][w][jj] - mu);
+      const int J = c * kChunk + jj;
+      const bool okJ = J < nJ;
+      float Mc = okJ ? m : -INFINITY;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) Mc = fmaxf(Mc, __shfl_xor(Mc, off, 32));
+      const float E = okJ ? S * __builtin_amdgcn_exp2f(m - Mc) : 0.f;
+      float tsum = E;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) tsum += __shfl_xor(tsum, off, 32);
+      if (okJ) row_out[J] = E;
+      if (jj == 0) {
+        cmax[c] = Mc;
+        csum[c] = tsum;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // global maximum and total over chunks (fixed order: per-lane strided,
+    // then a butterfly), in float64
+    double M = -INFINITY;
+    for (int c = lane; c < nch; c += 64) M = fmax(M, (double)cmax[c]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmax(M, __shfl_xor(M, off));
+    double tot = 0.0;
+    for (int c = lane; c < nch; c += 64) tot += (double)csum[c] * exp2((double)cmax[c] - M);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+    if (half == 0) {
+      // each of these lanes rescales only the entries it wrote itself
+      const double inv = 1.0 / tot;
+      for (int c = 0; c < nch; ++c) {
+        const int J = c * kChunk + jj;
+        if (J < nJ)
+          row_out[J] = (float)((double)row_out[J] * exp2((double)cmax[c] - M) * inv);
+      }
+    }
+  }
+}
+
+template <int DT, int D, int RT, int NW>
+static hipError_t launch_scores_t(const Plan& p, const void* q, const float* kbar, float c2,
+                                  float* scores, hipStream_t st) {
+  const int nch = (p.max_nblk + kChunk - 1) / kChunk;
+  const size_t lds = sizeof(float) * 2 * nch;
+  hipLaunchKernelGGL((scores_mfma_kernel<DT, D, RT, NW>), dim3((unsigned)p.num_segments),
+                     dim3(NW * 64), lds, st, p, (const typename Elem<DT>::T*)q, kbar, c2, scores);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+static hipError_t launch_scores_d(const Plan& p, const void* q, const float* kbar, float c2,
+                                  float* scores, hipStream_t st) {
+  const int rmax = p.g * p.B;
+  if (rmax <= 128) return launch_scores_t<DT, D, 1, 4>(p, q, kbar, c2, scores, st);
+  if (rmax <= 256) return launch_scores_t<DT, D, 2, 4>(p, q, kbar, c2, scores, st);
+  if (rmax <= 512) return launch_scores_t<DT, D, 2, 8>(p, q, kbar, c2, scores, st);
+  return launch_scores_t<DT, D, 4, 8>(p, q, kbar, c2, scores, st);
+}
+
+bool scores_mfma_supported(const Plan& p, int dtype) {
+  return (dtype == kBF16 || dtype == kFP8) && p.g * p.B <= 1024;
+}
+
+hipError_t launch_scores_mfma(const Plan& p, int dtype, const void* q, const float* kbar,
+                              float c2, float* scores, hipStream_t st) {
+  if (p.num_segments == 0) return hipSuccess;
+  if (dtype == kBF16)
+    return p.d == 128 ? launch_scores_d<kBF16, 128>(p, q, kbar, c2, scores, st)
+                      : launch_scores_d<kBF16, 64>(p, q, kbar, c2, scores, st);
+  return p.d == 128 ? launch_scores_d<kFP8, 128>(p, q, kbar, c2, scores, st)
+                    : launch_scores_d<kFP8, 64>(p, q, kbar, c2, scores, st);
+}
+
+}  // namespace bslp
