@@ -177,7 +177,7 @@ def main():
         if ev is not None:
             ev[2].record(stream)
         bslp.sparse_prefill_attn(prob, params, q, k, v, bufs.kbar, bufs.vbar, bufs.cu, bufs.idx,
-                                 bufs.out, bufs.lse, sp)
+                                 bufs.out, bufs.lse, bufs.workspace, sp)
         if ev is not None:
             ev[3].record(stream)
 

@@ -68,6 +68,7 @@ class Sizes(ctypes.Structure):
         ("pooled_rows", ctypes.c_int64),
         ("score_elems", ctypes.c_int64),
         ("num_segments", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -92,7 +93,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bslp_block_scores.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, vp]
     lib.bslp_select_blocks.argtypes = [P(Problem), P(SelectParams), vp, vp, vp, vp, vp]
     lib.bslp_sparse_prefill_attn.argtypes = [P(Problem), P(SelectParams), vp, vp, vp, vp, vp,
-                                             vp, vp, vp, vp, vp]
+                                             vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     for name in ("bslp_get_sizes", "bslp_block_scores", "bslp_select_blocks",
                  "bslp_sparse_prefill_attn"):
         getattr(lib, name).restype = ctypes.c_int
@@ -170,11 +171,15 @@ def select_blocks(problem, params, scores, counts, cu, idx, stream=None):
 
 
 def sparse_prefill_attn(problem, params, q, k, v, kbar, vbar, cu, idx, out, lse=None,
-                        stream=None):
+                        workspace=None, stream=None):
+    """`workspace`: a device tensor of at least get_sizes(problem).workspace_bytes
+    bytes (None passes a NULL pointer and size 0)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().bslp_sparse_prefill_attn(ctypes.byref(problem), ctypes.byref(params),
                                                    _ptr(q), _ptr(k), _ptr(v), _ptr(kbar),
                                                    _ptr(vbar), _ptr(cu), _ptr(idx), _ptr(out),
-                                                   _ptr(lse), _stream(stream)))
+                                                   _ptr(lse), _ptr(workspace), nbytes,
+                                                   _stream(stream)))
 
 
 class Buffers:
@@ -196,6 +201,7 @@ class Buffers:
         odt = f32 if problem.dtype == F32 else torch.bfloat16
         self.out = torch.empty((T, hq, d), dtype=odt, device=device)
         self.lse = torch.empty((hq, T), dtype=f32, device=device)
+        self.workspace = torch.empty(max(16, s.workspace_bytes), dtype=torch.uint8, device=device)
 
 
 def prefill(problem, params, q, k, v, bufs: Buffers | None = None, stream=None) -> Buffers:
@@ -204,7 +210,7 @@ def prefill(problem, params, q, k, v, bufs: Buffers | None = None, stream=None) 
     block_scores(problem, q, k, v, bufs.kbar, bufs.vbar, bufs.scores, stream)
     select_blocks(problem, params, bufs.scores, bufs.counts, bufs.cu, bufs.idx, stream)
     sparse_prefill_attn(problem, params, q, k, v, bufs.kbar, bufs.vbar, bufs.cu, bufs.idx,
-                        bufs.out, bufs.lse, stream)
+                        bufs.out, bufs.lse, bufs.workspace, stream)
     return bufs
 
 

@@ -88,6 +88,15 @@ bslp_status build_plan(const bslp_problem* pr, bslp::Plan* plan, bslp::KVDesc* k
       return fail(BSLP_ERR_UNSUPPORTED, "problem exceeds 2^31 tokens or index entries");
   }
   plan->max_nblk = max_nblk;
+  // heaviest requests first (stable insertion sort, at most 64 entries)
+  for (int i = 0; i < pr->num_seqs; ++i) {
+    int j = i;
+    while (j > 0 && plan->seq[plan->order[j - 1]].nblk < plan->seq[i].nblk) {
+      plan->order[j] = plan->order[j - 1];
+      --j;
+    }
+    plan->order[j] = i;
+  }
   plan->total_tokens = tok;
   plan->pooled_rows = pool;
   plan->num_segments = seg;
@@ -133,6 +142,7 @@ bslp_status bslp_get_sizes(const bslp_problem* problem, bslp_sizes* out) {
   out->pooled_rows = plan.pooled_rows;
   out->score_elems = plan.score_elems;
   out->num_segments = plan.num_segments;
+  out->workspace_bytes = (int64_t)bslp::attn_workspace_bytes(plan);
   return BSLP_OK;
 }
 
@@ -174,7 +184,8 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
                                      const bslp_select_params* params, const void* q,
                                      const void* k, const void* v, const float* kbar,
                                      const float* vbar, const int32_t* cu, const int32_t* idx,
-                                     void* out, float* lse, void* stream) {
+                                     void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
   bslp::Plan plan;
   bslp::KVDesc kv;
   bslp::SelectArgs sa;
@@ -185,7 +196,15 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
   if (plan.total_tokens == 0) return BSLP_OK;
   if (!q || !k || !v || !kbar || !vbar || !cu || !idx || !out)
     return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
-  bslp::AttnArgs a{q, k, v, kbar, vbar, cu, idx, out, lse,
+  const size_t need = bslp::attn_workspace_bytes(plan);
+  if (workspace_bytes < need)
+    return fail(BSLP_ERR_INVALID_ARG, "workspace_bytes " + std::to_string(workspace_bytes) +
+                                          " is below the " + std::to_string(need) +
+                                          " bytes bslp_get_sizes reports");
+  if (need > 0 && !workspace) return fail(BSLP_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(BSLP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  bslp::AttnArgs a{q, k, v, kbar, vbar, cu, idx, out, lse, workspace,
                    problem->softmax_scale * problem->q_scale, problem->k_scale,
                    problem->v_scale, sa.correction};
   // bf16 runs on the matrix cores; float32 keeps exact fp32 arithmetic on the

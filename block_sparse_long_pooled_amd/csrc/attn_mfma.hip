@@ -3,31 +3,40 @@
 // Sec. 3.1 last sentence, Sec. 3.2 / Fig. 3 correction path, PackGQA, CSR
 // and paged-KV paragraphs).  Written for gfx950 wave64 MFMA.
 //
-// Work unit: (segment (b, h, I), 128 consecutive PackGQA rows of tile I);
-// 4 waves x 32 rows.  Packed row r of the tile is position I*B + r / g of
-// query head h*g + r % g, so one staged K/V block serves all g heads.
+// Work unit.  (segment (b, h, I), 32*RT*NW consecutive PackGQA rows of tile
+// I), one workgroup of NW waves x RT row tiles of 32 rows (RT = 1 keeps a
+// wave within 256 VGPRs, so two waves share each SIMD).  Packed row r of the tile is
+// position I*B + r / g of query head h*g + r % g, so every staged K/V key
+// serves all g heads of the group.  Units are enumerated heaviest first
+// (longest request first, tiles in descending I) with the KV head innermost,
+// so consecutive workgroups - which the dispatcher spreads over the XCDs
+// round robin - keep one KV head per XCD and its L2.
 //
-// Per wave the scores are computed transposed, S^T[key, row] = K Q^T, with
-// v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims of K (from LDS), B = the
-// wave's Q rows (kept in registers).  In the 32x32 accumulator every lane
-// then owns one query row (column) and 16 keys, the other 16 keys of the
-// 32-key tile sitting in lane ^ 32; row max and row sum are in-lane plus one
-// v_permlane32_swap.  The probabilities stay in registers and feed the PV
-// product O^T[d, row] += V^T P^T as the B operand directly: the 8 values a
-// lane holds for 16 consecutive keys are keys {0-3, 8-11} (lanes 0-31) or
-// {4-7, 12-15} (lanes 32-63), so V^T is staged in LDS with its key columns
-// permuted the same way, and every MFMA operand is one 16-byte LDS read.
+// Pipeline.  The unit's work is a uniform sequence of 64-key steps: the
+// selected blocks from the CSR list walked backwards (B/64 steps each), then
+// the correction chunks of 64 pooled blocks that hold at least one block of
+// todo = valid & ~selected (valid = J <= I-1, fully visible to the tile).
+// Every thread derives the same sequence, so no step needs a vote.  Step n+1
+// is fetched from global memory into registers while step n is multiplied
+// out of LDS; the registers are then written to the other LDS buffer, and one
+// barrier per step publishes it.
 //
-// LDS layout (bytes): K tile [BLK][D] bf16 and V^T tile [D][BLK] bf16, both
-// in 16-byte units XOR-swizzled by row so that the 32 lanes of an operand read
-// and the transposing writes hit distinct banks; plus a selected-block bitmap
-// for the correction chunks.
+// MFMA layout.  Per wave S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32
+// keys x 16 dims of K from LDS, B = the wave's 32 query rows from
+// registers): every lane owns one query row and 16 keys of each 32-key tile,
+// the other 16 being in lane ^ 32, so the row max and row sum are in-lane plus
+// one v_permlane32_swap.  The probabilities feed O^T += V^T P^T straight from
+// registers as the B operand: the 8 values a lane holds for 16 consecutive
+// keys are keys {0-3, 8-11} (lanes 0-31) or {4-7, 12-15} (lanes 32-63), so
+// V^T is stored in LDS with its key columns permuted the same way and each
+// A operand is one 16-byte LDS read.  K and V^T rows are padded by 16 bytes
+// so the operand reads of 16 lanes fall in distinct banks.
 //
-// Selected blocks are walked backwards (CSR order reversed); the pruned blocks
-// that every row of the tile sees completely (J <= I-1, not selected) then
-// enter in chunks of BLK pooled keys kbar_J / values vbar_J through the same
-// MFMA pipeline, their logits shifted by log|B_J| and unselected or invisible
-// columns masked; chunks without such blocks are skipped uniformly.
+// Softmax.  Scores stay unscaled in the accumulator; with c = scale*log2(e),
+// p = exp2(s*c - m) is one FMA and one v_exp_f32.  The running maximum m is
+// raised only when a step exceeds it by more than 8 (so p < 2^8), which makes
+// the output rescale rare.  Correction terms enter as s*c + log2|B_J| with
+// unselected or invisible columns at -inf.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -38,21 +47,15 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRows = 128;  // packed query rows per unit
-constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kKeys = 64;  // keys per pipeline step
 constexpr float kLn2 = 0.6931471805599453f;
+
+enum StepKind : int { kExact = 0, kCorr = 1, kDone = 2 };
 
 __device__ __forceinline__ int kperm(int key) {  // V^T column of a key
   return (key & ~15) | ((key & 4) << 1) | ((key & 8) >> 1) | (key & 3);
 }
-__device__ __forceinline__ int kswz(int key) { return key & 7; }
-__device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
 
-// v_permlane32_swap exchanges the src0 of lanes 0-31 with the vdst of lanes
-// 32-63; with both operands = x every lane ends up holding {own x, x of
-// lane ^ 32} in its two results (order depending on the half), so max / sum
-// of the pair combine the two halves of a row in every lane.
 __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
@@ -72,349 +75,515 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-}  // namespace
-
-template <int D, int BLK>
-struct MfmaTile {
-  static constexpr int KT = BLK / 32;    // 32-key tiles of S^T
-  static constexpr int KS = D / 16;      // k-steps of Q K^T
-  static constexpr int DT = D / 32;      // 32-dim tiles of O^T
-  static constexpr int PT = BLK / 16;    // k-steps of P V
-  static constexpr int KU = D / 8;       // 16-byte units per K row
-  static constexpr int VU = BLK / 8;     // 16-byte units per V^T row
-  static constexpr int KTOTAL = BLK * KU;        // 16-byte K chunks per tile
-  static constexpr int VTOTAL = (BLK / 4) * KU;  // 4-key x 8-dim V groups per tile
-  static constexpr int KCHUNKS = (KTOTAL + kThreads - 1) / kThreads;
-  static constexpr int VGROUPS = (VTOTAL + kThreads - 1) / kThreads;
+// One step of the unit's sequence.
+struct Step {
+  int kind;  // StepKind
+  int t;     // exact: CSR position
+  int hf;    // exact: 64-key half of the block
+  int c;     // correction: chunk of 64 pooled blocks
 };
 
-// K tile: element (key, d) at key*D + ((d/8) ^ kswz(key))*8 + d%8
-// V^T tile: element (d, key) at d*BLK + ((kperm(key)/8) ^ vswz(d))*8 + kperm(key)%8
+struct UnitCtx {
+  int b, h, I, len, tok_start, pool_base, B, beg, end;
+};
 
-template <int D, int BLK>
-__device__ __forceinline__ void store_k_unit(uint16_t* Ks, int key, int unit, uint4 val) {
-  *reinterpret_cast<uint4*>(Ks + key * D + ((unit ^ kswz(key)) << 3)) = val;
-}
-
-// 4 consecutive keys (4a .. 4a+3) x 8 dims (8e .. 8e+7) -> V^T rows 8e..8e+7.
-template <int D, int BLK>
-__device__ __forceinline__ void store_v_group(uint16_t* Vt, int a, int e, const uint4 (&w)[4]) {
-  const int col = kperm(4 * a);  // 4-aligned, the 4 keys stay adjacent
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&w[0]);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&w[1]);
-  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&w[2]);
-  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&w[3]);
+// todo bits of correction chunk c (blocks 64c .. 64c+63, valid J <= I-1).
+__device__ __forceinline__ uint64_t chunk_todo(const uint32_t* selbits, int c, int I) {
+  uint64_t bits = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;  // high / low halves
-    const uint32_t lo = __builtin_amdgcn_perm(w1[i >> 1], w0[i >> 1], sel);
-    const uint32_t hi = __builtin_amdgcn_perm(w3[i >> 1], w2[i >> 1], sel);
-    const int d = 8 * e + i;
-    uint16_t* dst = Vt + d * BLK + ((((col >> 3) ^ vswz(d))) << 3) + (col & 7);
-    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  for (int w = 0; w < 2; ++w) {
+    const int J0 = 64 * c + 32 * w;
+    const int nv = min(max(I - J0, 0), 32);
+    if (nv == 0) continue;
+    const uint32_t m = nv >= 32 ? 0xffffffffu : ((1u << nv) - 1u);
+    bits |= (uint64_t)(~selbits[2 * c + w] & m) << (32 * w);
   }
+  return bits;
 }
 
-// Stage exact key block: keys j0 .. j0+cnt-1 of request b, head h.
-template <int D, int BLK>
-__device__ __forceinline__ void stage_kv_block(uint16_t* Ks, uint16_t* Vt, const uint16_t* k,
-                                               const uint16_t* v, const KVDesc& kv, int b,
-                                               int tok_start, int hkv, int h, int j0, int cnt) {
-  using C = MfmaTile<D, BLK>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < C::KCHUNKS; ++i) {
-    const int c = tid + i * kThreads;
-    if (C::KTOTAL % kThreads != 0 && c >= C::KTOTAL) break;
-    const int key = c / C::KU, unit = c % C::KU;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (key < cnt) {
-      const int64_t row = kv.row(b, tok_start, j0 + key);
-      val = *reinterpret_cast<const uint4*>(k + (row * hkv + h) * D + unit * 8);
+__device__ __forceinline__ void find_chunk(Step& st, const uint32_t* selbits, int I) {
+  while (64 * st.c < I && chunk_todo(selbits, st.c, I) == 0) ++st.c;
+  st.kind = 64 * st.c < I ? kCorr : kDone;
+}
+
+// First step, or the step after `st`.  Identical in every thread.
+__device__ __forceinline__ void advance(Step& st, const UnitCtx& u, const int32_t* idx,
+                                        const uint32_t* selbits, int correction) {
+  const int halves = u.B / kKeys;
+  if (st.kind == kExact) {
+    for (;;) {
+      if (++st.hf == halves) {
+        st.hf = 0;
+        --st.t;
+      }
+      if (st.t < u.beg) break;
+      const int key0 = idx[st.t] * u.B + st.hf * kKeys;
+      if (key0 < u.len) return;  // skip halves past the end of a short last block
     }
-    store_k_unit<D, BLK>(Ks, key, unit, val);
+    st.kind = kCorr;
+    st.c = -1;
   }
+  if (st.kind == kCorr) {
+    if (!correction || u.I == 0) {
+      st.kind = kDone;
+      return;
+    }
+    ++st.c;
+    find_chunk(st, selbits, u.I);
+  }
+}
+
+__device__ __forceinline__ Step first_step(const UnitCtx& u, const int32_t* idx,
+                                           const uint32_t* selbits, int correction) {
+  Step st{kExact, u.end - 1, -1, 0};
+  if (u.end > u.beg) {
+    st.hf = 0;
+    return st;  // the last selected block always starts inside the request
+  }
+  st.kind = kCorr;
+  st.c = -1;
+  advance(st, u, idx, selbits, correction);
+  return st;
+}
+
+}  // namespace
+
+template <int D, int NW, int RT>
+struct AttnCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int ROWS = NW * RT * 32;  // packed rows per unit
+  static constexpr int KS = D / 16;          // k-steps of Q K^T
+  static constexpr int DT = D / 32;          // 32-dim tiles of O^T
+  static constexpr int KU = D / 8;           // 16-byte units per key row
+  static constexpr int KUN = kKeys * KU;     // K units per step
+  static constexpr int VPN = kKeys / 2 * KU; // V (key pair x unit) groups per step
+  static constexpr int KL = (KUN + NT - 1) / NT;
+  static constexpr int VL = (VPN + NT - 1) / NT;
+  static constexpr int KLD = D + 8;          // padded K row (bf16)
+  static constexpr int VLD = kKeys + 8;      // padded V^T row (bf16)
+};
+
+template <int D, int NW, int RT>
+struct Prefetch {
+  uint4 k[AttnCfg<D, NW, RT>::KL];
+  uint4 v[AttnCfg<D, NW, RT>::VL][2];
+};
+
+// Global -> registers for one step.  Exact steps read tokens key0.. of the
+// request (through the page table when K/V are paged); correction steps read
+// bf16 pooled rows.  Keys past the step's end (the short last block, the
+// last correction chunk) re-read the last valid row: their scores are masked,
+// so only finiteness matters, and the loads need no branch.
+template <int D, int NW, int RT>
+__device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf, const Step& st,
+                                           const UnitCtx& u, const KVDesc& kv, int hkv,
+                                           const uint16_t* k, const uint16_t* v,
+                                           const uint16_t* kb16, const uint16_t* vb16,
+                                           const int32_t* idx) {
+  using C = AttnCfg<D, NW, RT>;
+  const int tid = threadIdx.x;
+  const bool exact = st.kind == kExact;
+  const int key0 = exact ? idx[st.t] * u.B + st.hf * kKeys : kKeys * st.c;
+  const int last = min(kKeys, (exact ? u.len : u.I) - key0) - 1;
+  const int64_t stride = (int64_t)hkv * D;
+  if (exact && kv.page_table != nullptr) {
+    const uint16_t* kh = k + (int64_t)u.h * D;
+    const uint16_t* vh = v + (int64_t)u.h * D;
 #pragma unroll
-  for (int i = 0; i < C::VGROUPS; ++i) {
-    const int s = tid + i * kThreads;
-    if (C::VTOTAL % kThreads != 0 && s >= C::VTOTAL) break;
-    const int a = s / C::KU, e = s % C::KU;
-    uint4 w[4];
+    for (int i = 0; i < C::KL; ++i) {
+      const int f = min(tid + i * C::NT, C::KUN - 1);
+      const int key = min(f / C::KU, last);
+      const int64_t row = kv.row(u.b, u.tok_start, key0 + key);
+      pf.k[i] = *reinterpret_cast<const uint4*>(kh + row * stride + (f % C::KU) * 8);
+    }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int key = 4 * a + c;
-      w[c] = make_uint4(0, 0, 0, 0);
-      if (key < cnt) {
-        const int64_t row = kv.row(b, tok_start, j0 + key);
-        w[c] = *reinterpret_cast<const uint4*>(v + (row * hkv + h) * D + e * 8);
+    for (int i = 0; i < C::VL; ++i) {
+      const int s = min(tid + i * C::NT, C::VPN - 1);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int key = min(2 * (s / C::KU) + c, last);
+        const int64_t row = kv.row(u.b, u.tok_start, key0 + key);
+        pf.v[i][c] = *reinterpret_cast<const uint4*>(vh + row * stride + (s % C::KU) * 8);
       }
     }
-    store_v_group<D, BLK>(Vt, a, e, w);
+  } else {
+    const int64_t row0 = exact ? (int64_t)u.tok_start + key0 : (int64_t)u.pool_base + key0;
+    const uint16_t* kh = (exact ? k : kb16) + row0 * stride + (int64_t)u.h * D;
+    const uint16_t* vh = (exact ? v : vb16) + row0 * stride + (int64_t)u.h * D;
+#pragma unroll
+    for (int i = 0; i < C::KL; ++i) {
+      const int f = min(tid + i * C::NT, C::KUN - 1);
+      const int key = min(f / C::KU, last);
+      pf.k[i] = *reinterpret_cast<const uint4*>(kh + key * stride + (f % C::KU) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < C::VL; ++i) {
+      const int s = min(tid + i * C::NT, C::VPN - 1);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int key = min(2 * (s / C::KU) + c, last);
+        pf.v[i][c] = *reinterpret_cast<const uint4*>(vh + key * stride + (s % C::KU) * 8);
+      }
+    }
   }
 }
 
-__device__ __forceinline__ uint4 f32x8_to_bf16x8(const float* p) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  return make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                    pack_bf16x2(b.z, b.w));
-}
-
-// Stage pooled rows J0 .. J0+n-1 (float32 kbar / vbar, rounded to bf16).
-template <int D, int BLK>
-__device__ __forceinline__ void stage_pooled(uint16_t* Ks, uint16_t* Vt, const float* kbar,
-                                             const float* vbar, int64_t row0, int hkv, int h,
-                                             int n) {
-  using C = MfmaTile<D, BLK>;
+// Registers -> LDS: K row-major, V transposed with permuted key columns; both
+// with padded rows so the 16-byte operand reads of 16 lanes hit distinct banks.
+template <int D, int NW, int RT>
+__device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, uint16_t* Ks,
+                                           uint16_t* Vt) {
+  using C = AttnCfg<D, NW, RT>;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < C::KCHUNKS; ++i) {
-    const int c = tid + i * kThreads;
-    if (C::KTOTAL % kThreads != 0 && c >= C::KTOTAL) break;
-    const int key = c / C::KU, unit = c % C::KU;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (key < n) val = f32x8_to_bf16x8(kbar + ((row0 + key) * hkv + h) * D + unit * 8);
-    store_k_unit<D, BLK>(Ks, key, unit, val);
+  for (int i = 0; i < C::KL; ++i) {
+    const int f = tid + i * C::NT;
+    if (C::KUN % C::NT != 0 && f >= C::KUN) break;
+    const int key = f / C::KU, un = f % C::KU;
+    *reinterpret_cast<uint4*>(Ks + key * C::KLD + un * 8) = pf.k[i];
   }
 #pragma unroll
-  for (int i = 0; i < C::VGROUPS; ++i) {
-    const int s = tid + i * kThreads;
-    if (C::VTOTAL % kThreads != 0 && s >= C::VTOTAL) break;
-    const int a = s / C::KU, e = s % C::KU;
-    uint4 w[4];
+  for (int i = 0; i < C::VL; ++i) {
+    const int s = tid + i * C::NT;
+    if (C::VPN % C::NT != 0 && s >= C::VPN) break;
+    const int a = s / C::KU, un = s % C::KU;
+    const int col = kperm(2 * a);  // even; the pair stays adjacent
+    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&pf.v[i][0]);
+    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&pf.v[i][1]);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int key = 4 * a + c;
-      w[c] = key < n ? f32x8_to_bf16x8(vbar + ((row0 + key) * hkv + h) * D + e * 8)
-                     : make_uint4(0, 0, 0, 0);
+    for (int dd = 0; dd < 8; ++dd) {
+      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t word = __builtin_amdgcn_perm(w1[dd >> 1], w0[dd >> 1], sel);
+      *reinterpret_cast<uint32_t*>(Vt + (8 * un + dd) * C::VLD + col) = word;
     }
-    store_v_group<D, BLK>(Vt, a, e, w);
   }
 }
 
-// One wave's S^T = K Q^T over the staged tile.
-template <int D, int BLK>
-__device__ __forceinline__ void qk_tile(const uint16_t* Ks, const bf16x8_t (&qf)[D / 16],
-                                        f32x16_t (&sacc)[BLK / 32], int lane) {
-  using C = MfmaTile<D, BLK>;
-#pragma unroll
-  for (int kt = 0; kt < C::KT; ++kt) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-  }
+enum Mode : int { kPlain = 0, kDiag = 1, kCorrMode = 2 };
+
+// One 64-key step of one wave over its RT row tiles: S^T = K Q^T, online
+// softmax, O^T += V^T P^T.  `mode` is uniform across the workgroup.
+template <int D, int NW, int RT>
+__device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t* Vt,
+                                             const bf16x8_t (&qf)[RT][D / 16],
+                                             f32x16_t (&oacc)[RT][D / 32], float (&m_run)[RT],
+                                             float (&l_run)[RT], float c, int mode, int key0,
+                                             int len, const int (&qpos)[RT], uint64_t todo,
+                                             float bias) {
+  using C = AttnCfg<D, NW, RT>;
+  const int lane = threadIdx.x & 63;
   const int key_l = lane & 31, half = lane >> 5;
+  f32x16_t sacc[RT][2];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[rt][kt][r] = 0.f;
+    }
+  }
+  const uint16_t* kbase = Ks + key_l * C::KLD + half * 8;
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt) {
-      const int key = kt * 32 + key_l;
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-          Ks + key * D + (((2 * ks + half) ^ kswz(key)) << 3));
-      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kt], 0, 0, 0);
+    for (int kt = 0; kt < 2; ++kt) {
+      const bf16x8_t a =
+          *reinterpret_cast<const bf16x8_t*>(kbase + kt * 32 * C::KLD + ks * 16);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        sacc[rt][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rt][ks], sacc[rt][kt], 0, 0, 0);
     }
   }
-}
-
-// Online softmax on the masked, scaled logits in sacc (log2 domain), then
-// O^T += V^T P^T.
-template <int D, int BLK>
-__device__ __forceinline__ void softmax_pv(const uint16_t* Vt, f32x16_t (&sacc)[BLK / 32],
-                                           f32x16_t (&oacc)[D / 32], float& m_run, float& l_run,
-                                           int lane) {
-  using C = MfmaTile<D, BLK>;
-  float mx = -INFINITY;
+  // masks: diagonal block (token causality and the request end) or the
+  // correction chunk's todo bits; branch-free per element, uniform per step
+  if (mode != kPlain) {
+    uint64_t bits;
+    if (mode == kDiag) {
+      const int nvis = len - key0;  // >= 1
+      bits = nvis >= 64 ? ~0ull : ((1ull << nvis) - 1ull);
+    } else {
+      bits = todo;
+    }
+    bits >>= 4 * half;  // the lane's keys are kk0 + 4*half
 #pragma unroll
-  for (int kt = 0; kt < C::KT; ++kt) {
+    for (int rt = 0; rt < RT; ++rt) {
+      const int lim = (mode == kDiag ? qpos[rt] - key0 : 63) - 4 * half;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-  }
-  mx = halves_max(mx);
-  const float m_new = fmaxf(m_run, mx);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-  float lsum = 0.f;
-  bf16x8_t pb[C::PT];
+      for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-  for (int t = 0; t < C::PT; ++t) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = __builtin_amdgcn_exp2f(sacc[t >> 1][8 * (t & 1) + j] - m_use);
-      lsum += p;
-      pb[t][j] = (__bf16)p;
+        for (int r = 0; r < 16; ++r) {
+          const int kk0 = kt * 32 + (r >> 2) * 8 + (r & 3);
+          const bool keep = ((bits >> kk0) & 1ull) && kk0 <= lim;
+          sacc[rt][kt][r] = keep ? sacc[rt][kt][r] : -INFINITY;
+        }
+      }
     }
   }
-  l_run = l_run * alpha + lsum;
-  m_run = m_new;
+  // online softmax in units of log2 (x = s*c, + log2|B_J| for pooled terms).
+  // The running maximum is raised only when the step's maximum exceeds it by
+  // more than 8, so probabilities stay below 2^8 and the output rescale is
+  // rare; the final normalisation uses the same reference, so it is exact.
+  const float cb = mode == kCorrMode ? bias : 0.f;
+  bf16x8_t pb[RT][4];
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) {
+  for (int rt = 0; rt < RT; ++rt) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rt][kt][r]);
+    }
+    mx = fmaf(halves_max(mx), c, cb);  // c > 0: the maximum commutes with the scale
+    if (mx > m_run[rt] + 8.f) {
+      const float alpha = m_run[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rt] - mx);
+      l_run[rt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[rt][dt][r] *= alpha;
+      }
+      m_run[rt] = mx;
+    }
+    const float moff = cb - (m_run[rt] == -INFINITY ? 0.f : m_run[rt]);
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rt][t >> 1][8 * (t & 1) + j], c, moff));
+        const float p1 =
+            __builtin_amdgcn_exp2f(fmaf(sacc[rt][t >> 1][8 * (t & 1) + j + 1], c, moff));
+        lsum += p0 + p1;
+        pb[rt][t][j] = (__bf16)p0;
+        pb[rt][t][j + 1] = (__bf16)p1;
+      }
+    }
+    l_run[rt] += lsum;
   }
-  const int d_l = lane & 31, half = lane >> 5;
+  const uint16_t* vbase = Vt + key_l * C::VLD + half * 8;
 #pragma unroll
-  for (int t = 0; t < C::PT; ++t) {
+  for (int t = 0; t < 4; ++t) {
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      const int d = dt * 32 + d_l;
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-          Vt + d * BLK + (((2 * t + half) ^ vswz(d)) << 3));
-      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], oacc[dt], 0, 0, 0);
+      const bf16x8_t a =
+          *reinterpret_cast<const bf16x8_t*>(vbase + dt * 32 * C::VLD + t * 16);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        oacc[rt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rt][t], oacc[rt][dt], 0, 0, 0);
     }
   }
 }
 
-template <int D, int BLK>
-__global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(
+template <int D, int NW, int RT>
+__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
     Plan p, KVDesc kv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ kbar,
-    const float* __restrict__ vbar, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ idx, float scale_log2, int correction, int units_per_seg,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ kb16,
+    const uint16_t* __restrict__ vb16, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ idx, float c, int correction, int units_per_seg,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
-  using C = MfmaTile<D, BLK>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * BLK];
+  using C = AttnCfg<D, NW, RT>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKeys * C::KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VLD];
   __shared__ uint32_t selbits[kMaxBlocksPerSeq / 32];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t unit = (int64_t)gridDim.x - 1 - blockIdx.x;  // longest rows first
-  const int64_t seg = unit / units_per_seg;
-  const int mt = (int)(unit % units_per_seg);
-  const int b = seq_of_segment(p, seg);
+  const int half = lane >> 5;
+
+  // ---- unit -> (request, tile I, row block mt, KV head h)
+  const int64_t unit = blockIdx.x;
+  int pos = 0;
+  while (pos + 1 < p.num_seqs && p.seq[p.order[pos + 1]].unit_base <= unit) ++pos;
+  const int b = p.order[pos];
   const SeqInfo s = p.seq[b];
-  const int local = (int)(seg - s.seg_base);
-  const int h = local / s.nblk;
-  const int I = local % s.nblk;
+  const int64_t local = unit - s.unit_base;
+  const int per_I = p.hkv * units_per_seg;
+  const int I = s.nblk - 1 - (int)(local / per_I);
+  const int rem = (int)(local % per_I);
+  const int mt = rem / p.hkv;
+  const int h = rem % p.hkv;
+  const int64_t seg = (int64_t)s.seg_base + (int64_t)h * s.nblk + I;
   const int nb = min(p.B, s.len - I * p.B);
   const int R = p.g * nb;
-  if (mt * kRows >= R) return;  // uniform
+  UnitCtx u{b, h, I, s.len, s.tok_start, s.pool_base, p.B, cu[seg], cu[seg + 1]};
 
-  // this lane's query row
-  const int r = mt * kRows + wave * 32 + (lane & 31);
-  const bool valid = r < R;
-  const int qpos = I * p.B + (valid ? r / p.g : 0);
-  const int hq = h * p.g + r % p.g;
-  const int half = lane >> 5;
-  bf16x8_t qf[C::KS];
-  {
-    const int64_t qoff = ((int64_t)(s.tok_start + qpos) * p.hq + hq) * D;
+  // ---- this lane's query rows (B operands of Q K^T), one per row tile
+  const int row0 = mt * C::ROWS + wave * RT * 32;
+  const bool wave_active = row0 < R;
+  int qpos[RT], hqs[RT];
+  bool valid[RT];
+  bf16x8_t qf[RT][C::KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = row0 + rt * 32 + (lane & 31);
+    valid[rt] = r < R;
+    qpos[rt] = I * p.B + (valid[rt] ? r / p.g : 0);
+    hqs[rt] = h * p.g + (valid[rt] ? r % p.g : 0);
+    const int64_t qoff = ((int64_t)(s.tok_start + qpos[rt]) * p.hq + hqs[rt]) * D;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (valid) u = *reinterpret_cast<const uint4*>(q + qoff + ks * 16 + half * 8);
-      qf[ks] = __builtin_bit_cast(bf16x8_t, u);
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (valid[rt]) w = *reinterpret_cast<const uint4*>(q + qoff + ks * 16 + half * 8);
+      qf[rt][ks] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
-  f32x16_t oacc[C::DT];
-#pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) {
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) oacc[dt][rr] = 0.f;
-  }
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16_t sacc[C::KT];
 
-  const int beg = cu[seg], end = cu[seg + 1];
-  for (int t = end - 1; t >= beg; --t) {
-    const int J = idx[t];
-    const int j0 = J * p.B;
-    const int cnt = min(BLK, s.len - j0);
-    __syncthreads();  // previous tile fully consumed
-    stage_kv_block<D, BLK>(Ks, Vt, k, v, kv, b, s.tok_start, p.hkv, h, j0, cnt);
-    __syncthreads();
-    qk_tile<D, BLK>(Ks, qf, sacc, lane);
-    const bool diag = (J == I);
-#pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt) {
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int key = kt * 32 + (rr >> 2) * 8 + half * 4 + (rr & 3);
-        float x = sacc[kt][rr] * scale_log2;
-        if (diag && (j0 + key > qpos || key >= cnt)) x = -INFINITY;
-        sacc[kt][rr] = x;
-      }
-    }
-    softmax_pv<D, BLK>(Vt, sacc, oacc, m_run, l_run, lane);
-  }
-
+  // ---- selected-block bitmap for the correction chunks
   if (correction && I > 0) {
     const int nwords = (I + 31) >> 5;
+    for (int w = tid; w < nwords; w += C::NT) selbits[w] = 0u;
     __syncthreads();
-    for (int w = tid; w < nwords; w += kThreads) selbits[w] = 0u;
-    __syncthreads();
-    for (int t = beg + tid; t < end; t += kThreads) {
+    for (int t = u.beg + tid; t < u.end; t += C::NT) {
       const int J = idx[t];
       if (J < I) atomicOr(&selbits[J >> 5], 1u << (J & 31));
     }
     __syncthreads();
-    const float bias = __log2f((float)p.B);  // every J <= I-1 is a full block
-    for (int J0 = 0; J0 < I; J0 += BLK) {
-      const int n = min(BLK, I - J0);
-      bool any = false;  // identical decision in every thread
-      for (int w = 0; w < (n + 31) / 32; ++w) {
-        const int rem = n - 32 * w;
-        const uint32_t validm = rem >= 32 ? 0xffffffffu : ((1u << rem) - 1u);
-        any |= ((~selbits[(J0 >> 5) + w]) & validm) != 0u;
-      }
-      if (!any) continue;
-      __syncthreads();
-      stage_pooled<D, BLK>(Ks, Vt, kbar, vbar, (int64_t)s.pool_base + J0, p.hkv, h, n);
-      __syncthreads();
-      qk_tile<D, BLK>(Ks, qf, sacc, lane);
-#pragma unroll
-      for (int kt = 0; kt < C::KT; ++kt) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int key = kt * 32 + (rr >> 2) * 8 + half * 4 + (rr & 3);
-          const int J = J0 + key;
-          const bool todo = key < n && !((selbits[J >> 5] >> (J & 31)) & 1u);
-          sacc[kt][rr] = todo ? sacc[kt][rr] * scale_log2 + bias : -INFINITY;
-        }
-      }
-      softmax_pv<D, BLK>(Vt, sacc, oacc, m_run, l_run, lane);
-    }
   }
 
-  // epilogue: l over all keys of the row = both lane halves
-  const float l_tot = halves_sum(l_run);
-  if (!valid) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int64_t ooff = ((int64_t)(s.tok_start + qpos) * p.hq + hq) * D;
+  f32x16_t oacc[RT][C::DT];
+  float m_run[RT], l_run[RT];
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) {
+  for (int rt = 0; rt < RT; ++rt) {
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = dt * 32 + g4 * 8 + half * 4;
-      const uint32_t lo = pack_bf16x2(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv);
-      const uint32_t hi = pack_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
-      *reinterpret_cast<uint2*>(out + ooff + d) = make_uint2(lo, hi);
+    for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) oacc[rt][dt][rr] = 0.f;
     }
   }
-  if (lse && half == 0)
-    lse[(int64_t)hq * p.total_tokens + s.tok_start + qpos] =
-        l_tot > 0.f ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
+  const float bias = __log2f((float)p.B);  // corrected blocks are full blocks
+
+  Prefetch<D, NW, RT> pf;
+  Step cur = first_step(u, idx, selbits, correction);
+  if (cur.kind != kDone) {
+    fetch_step<D, NW, RT>(pf, cur, u, kv, p.hkv, k, v, kb16, vb16, idx);
+    store_step<D, NW, RT>(pf, Ks[0], Vt[0]);
+  }
+  Step nxt = cur;
+  if (cur.kind != kDone) advance(nxt, u, idx, selbits, correction);
+  if (nxt.kind != kDone) fetch_step<D, NW, RT>(pf, nxt, u, kv, p.hkv, k, v, kb16, vb16, idx);
+  __syncthreads();
+  int buf = 0;
+  while (cur.kind != kDone) {
+    if (wave_active) {
+      int mode, key0 = 0;
+      uint64_t todo = 0;
+      if (cur.kind == kExact) {
+        const int J = idx[cur.t];
+        key0 = J * p.B + cur.hf * kKeys;
+        mode = J == I ? kDiag : kPlain;
+      } else {
+        mode = kCorrMode;
+        todo = chunk_todo(selbits, cur.c, I);
+      }
+      compute_step<D, NW, RT>(Ks[buf], Vt[buf], qf, oacc, m_run, l_run, c, mode, key0, s.len,
+                              qpos, todo, bias);
+    }
+    if (nxt.kind != kDone) store_step<D, NW, RT>(pf, Ks[buf ^ 1], Vt[buf ^ 1]);
+    __syncthreads();
+    cur = nxt;
+    if (nxt.kind != kDone) {
+      advance(nxt, u, idx, selbits, correction);
+      if (nxt.kind != kDone) fetch_step<D, NW, RT>(pf, nxt, u, kv, p.hkv, k, v, kb16, vb16, idx);
+    }
+    buf ^= 1;
+  }
+
+  // ---- epilogue: l over all keys of the row = both lane halves
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float l_tot = halves_sum(l_run[rt]);
+    if (!valid[rt]) continue;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int64_t ooff = ((int64_t)(s.tok_start + qpos[rt]) * p.hq + hqs[rt]) * D;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dt * 32 + g4 * 8 + half * 4;
+        const uint32_t lo =
+            pack_bf16x2(oacc[rt][dt][4 * g4] * inv, oacc[rt][dt][4 * g4 + 1] * inv);
+        const uint32_t hi =
+            pack_bf16x2(oacc[rt][dt][4 * g4 + 2] * inv, oacc[rt][dt][4 * g4 + 3] * inv);
+        *reinterpret_cast<uint2*>(out + ooff + d) = make_uint2(lo, hi);
+      }
+    }
+    if (lse && half == 0)
+      lse[(int64_t)hqs[rt] * p.total_tokens + s.tok_start + qpos[rt]] =
+          l_tot > 0.f ? m_run[rt] * kLn2 + __logf(l_tot) : -INFINITY;
+  }
 }
 
-template <int D, int BLK>
-static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs& a,
+// float32 pooled means -> bf16 (round to nearest even) for the correction
+// steps; n8 = number of 8-element groups.
+__global__ __launch_bounds__(256) void pooled_to_bf16_kernel(const float* __restrict__ kbar,
+                                                            const float* __restrict__ vbar,
+                                                            int64_t n8, uint16_t* __restrict__ kb16,
+                                                            uint16_t* __restrict__ vb16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * n8) return;
+  const bool is_v = i >= n8;
+  const int64_t j = is_v ? i - n8 : i;
+  const float* src = (is_v ? vbar : kbar) + 8 * j;
+  const float4 a = *reinterpret_cast<const float4*>(src);
+  const float4 bq = *reinterpret_cast<const float4*>(src + 4);
+  const uint4 w = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
+                             pack_bf16x2(bq.x, bq.y), pack_bf16x2(bq.z, bq.w));
+  *reinterpret_cast<uint4*>((is_v ? vb16 : kb16) + 8 * j) = w;
+}
+
+size_t attn_workspace_bytes(const Plan& p) {
+  const size_t n = (size_t)p.pooled_rows * p.hkv * p.d;  // elements per pooled tensor
+  return 2 * n * sizeof(uint16_t);
+}
+
+template <int D, int NW, int RT>
+static hipError_t launch_bf16_t(const Plan& p, const KVDesc& kv, const AttnArgs& a,
                                 hipStream_t st) {
-  const int units_per_seg = (p.g * p.B + kRows - 1) / kRows;
-  const int64_t units = p.num_segments * units_per_seg;
-  if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_mfma_bf16_kernel<D, BLK>), dim3((unsigned)units), dim3(kThreads), 0,
-                     st, p, kv, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     a.kbar, a.vbar, a.cu, a.idx, a.lscale * kLog2e, a.correction, units_per_seg,
+  const int rows = AttnCfg<D, NW, RT>::ROWS;
+  const int units_per_seg = (p.g * p.B + rows - 1) / rows;
+  // enumerate units: longest request first, tiles in descending I, then row
+  // block, KV head innermost
+  Plan pl = p;
+  int64_t base = 0;
+  for (int i = 0; i < pl.num_seqs; ++i) {
+    const int b = pl.order[i];
+    pl.seq[b].unit_base = (int32_t)base;
+    base += (int64_t)pl.seq[b].nblk * pl.hkv * units_per_seg;
+  }
+  if (base == 0) return hipSuccess;
+  const size_t n = (size_t)p.pooled_rows * p.hkv * p.d;
+  uint16_t* kb16 = reinterpret_cast<uint16_t*>(a.workspace);
+  uint16_t* vb16 = kb16 + n;
+  if (n > 0) {
+    const int64_t n8 = (int64_t)(n / 8);
+    hipLaunchKernelGGL(pooled_to_bf16_kernel, dim3((unsigned)((2 * n8 + 255) / 256)), dim3(256),
+                       0, st, a.kbar, a.vbar, n8, kb16, vb16);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, RT>), dim3((unsigned)base), dim3(NW * 64), 0, st,
+                     pl, kv, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)kb16, (const uint16_t*)vb16, a.cu, a.idx,
+                     a.lscale * 1.4426950408889634f, a.correction, units_per_seg,
                      (uint16_t*)a.out, a.lse);
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_bf16_d(const Plan& p, const KVDesc& kv, const AttnArgs& a,
+                                hipStream_t st) {
+  const int rows = p.g * p.B;
+  if (rows >= 256) return launch_bf16_t<D, 8, 1>(p, kv, a, st);
+  if (rows >= 128) return launch_bf16_t<D, 4, 1>(p, kv, a, st);
+  return launch_bf16_t<D, 2, 1>(p, kv, a, st);
+}
+
 hipError_t launch_attn_mfma_bf16(const Plan& p, const KVDesc& kv, const AttnArgs& a,
                                  hipStream_t st) {
-  if (p.d == 128 && p.B == 128) return launch_mfma_t<128, 128>(p, kv, a, st);
-  if (p.d == 128 && p.B == 64) return launch_mfma_t<128, 64>(p, kv, a, st);
-  if (p.d == 64 && p.B == 128) return launch_mfma_t<64, 128>(p, kv, a, st);
-  return launch_mfma_t<64, 64>(p, kv, a, st);
+  return p.d == 128 ? launch_bf16_d<128>(p, kv, a, st) : launch_bf16_d<64>(p, kv, a, st);
 }
 
 }  // namespace bslp

@@ -31,6 +31,7 @@ struct Plan {
   int32_t max_nblk;
   int64_t total_tokens, pooled_rows, score_elems, num_segments;
   SeqInfo seq[kMaxSeqs];
+  int32_t order[kMaxSeqs];  // requests by descending block count (ties: packed order)
 };
 
 // Where key/value token j of request b lives.

@@ -16,6 +16,7 @@ struct AttnArgs {
   const int32_t* idx;
   void* out;
   float* lse;
+  void* workspace;  // attn_workspace_bytes(plan) bytes, device
   float lscale;   // softmax_scale * q_scale
   float k_scale;  // 1 unless fp8
   float v_scale;
@@ -38,6 +39,9 @@ hipError_t launch_select(const Plan& p, const SelectArgs& a, const float* scores
 
 hipError_t launch_attn_valu(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
                             hipStream_t st);
+
+// Device scratch the attention launch needs (bf16 copies of the pooled means).
+size_t attn_workspace_bytes(const Plan& p);
 
 hipError_t launch_attn_mfma_bf16(const Plan& p, const KVDesc& kv, const AttnArgs& a,
                                  hipStream_t st);

@@ -110,6 +110,7 @@ typedef struct bslp_sizes {
   int64_t pooled_rows;  /* sum N_b: rows of kbar / vbar                       */
   int64_t score_elems;  /* sum Hkv N_b (N_b+1)/2: scores and idx capacity     */
   int64_t num_segments; /* sum Hkv N_b: entries of counts (cu has one more)   */
+  int64_t workspace_bytes; /* device scratch bslp_sparse_prefill_attn needs     */
 } bslp_sizes;
 
 /* Validates `problem` and fills `out`.  Host only; no HIP call. */
@@ -159,12 +160,17 @@ bslp_status bslp_select_blocks(const bslp_problem* problem, const bslp_select_pa
  * out: [T, Hq, d], float32 for BSLP_F32 else bfloat16.  lse: float32
  * [Hq, T] or NULL.  A row that sees no key gets O = 0 and LSE = -inf.
  * kbar / vbar / cu / idx are the outputs of stages 1 and 2 for the same
- * problem.  Only params->mean_correction is read. */
+ * problem.  Only params->mean_correction is read.
+ * workspace: device scratch of at least bslp_sizes.workspace_bytes bytes,
+ * 16-byte aligned, owned by the caller; its contents on entry do not matter
+ * and are overwritten (the call keeps lower-precision copies of kbar / vbar
+ * there).  Calls that overlap in time must not share a workspace. */
 bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
                                      const bslp_select_params* params, const void* q,
                                      const void* k, const void* v, const float* kbar,
                                      const float* vbar, const int32_t* cu, const int32_t* idx,
-                                     void* out, float* lse, void* stream);
+                                     void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* bslp_status_string(bslp_status status);

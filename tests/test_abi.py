@@ -43,6 +43,8 @@ def test_sizes_match_the_layout():
     assert s.pooled_rows == sum(N)
     assert s.num_segments == 2 * sum(N)
     assert s.score_elems == 2 * sum(n * (n + 1) // 2 for n in N)
+    # bf16 copies of the pooled keys and values for the correction steps
+    assert s.workspace_bytes == 2 * s.pooled_rows * 2 * 128 * 2
 
 
 def _status(fn):
@@ -75,14 +77,22 @@ def test_problem_validation(kw, status):
 class FakeTensor:
     """Stands in for a device tensor: a pointer that is never dereferenced."""
 
-    def __init__(self, shape=(4, 4)):
+    def __init__(self, shape=(4, 4), nbytes=16, ptr=0x1000):
         self.shape = shape
+        self.nbytes = nbytes
+        self.ptr = ptr
 
     def is_contiguous(self):
         return True
 
     def data_ptr(self):
-        return 0x1000
+        return self.ptr
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
 
 
 def test_page_table_validation():
@@ -137,3 +147,21 @@ def test_status_strings():
     assert lib.bslp_status_string(0) == b"ok"
     assert lib.bslp_status_string(2) == b"unsupported"
     assert isinstance(lib.bslp_last_error(), bytes)
+
+
+def test_attention_workspace_validated_before_launch():
+    p = _problem()
+    need = bslp.get_sizes(p).workspace_bytes
+    params = bslp.make_params(0.05)
+    t = FakeTensor()
+    st, d = _status(lambda: bslp.sparse_prefill_attn(p, params, t, t, t, t, t, t, t, t, t,
+                                                     workspace=FakeTensor(nbytes=need - 1),
+                                                     stream=0))
+    assert st == 1 and "workspace" in d
+    st, d = _status(lambda: bslp.sparse_prefill_attn(p, params, t, t, t, t, t, t, t, t, t,
+                                                     workspace=None, stream=0))
+    assert st == 1 and "workspace" in d
+    st, d = _status(lambda: bslp.sparse_prefill_attn(
+        p, params, t, t, t, t, t, t, t, t, t,
+        workspace=FakeTensor(nbytes=need, ptr=0x1008), stream=0))
+    assert st == 1 and "aligned" in d
