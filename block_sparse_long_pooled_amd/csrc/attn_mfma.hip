@@ -44,6 +44,7 @@ namespace bslp {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16 bytes, kept in registers
 
 namespace {
 
@@ -165,15 +166,18 @@ struct AttnCfg {
 
 template <int D, int NW, int RT>
 struct Prefetch {
-  uint4 k[AttnCfg<D, NW, RT>::KL];
-  uint4 v[AttnCfg<D, NW, RT>::VL][2];
+  u32x4_t k[AttnCfg<D, NW, RT>::KL];
+  u32x4_t v0[AttnCfg<D, NW, RT>::VL];  // key 2a of the pair
+  u32x4_t v1[AttnCfg<D, NW, RT>::VL];  // key 2a + 1
 };
 
 // Global -> registers for one step.  Exact steps read tokens key0.. of the
 // request (through the page table when K/V are paged); correction steps read
 // bf16 pooled rows.  Keys past the step's end (the short last block, the
 // last correction chunk) re-read the last valid row: their scores are masked,
-// so only finiteness matters, and the loads need no branch.
+// so only finiteness matters, and the loads need no branch.  Row indices are
+// resolved first and every load is issued from one place, so the values stay
+// in registers while they are in flight.
 template <int D, int NW, int RT>
 __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf, const Step& st,
                                            const UnitCtx& u, const KVDesc& kv, int hkv,
@@ -181,50 +185,48 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf, const Step& 
                                            const uint16_t* kb16, const uint16_t* vb16,
                                            const int32_t* idx) {
   using C = AttnCfg<D, NW, RT>;
+  constexpr int PAIRS = kKeys / 2;
   const int tid = threadIdx.x;
   const bool exact = st.kind == kExact;
   const int key0 = exact ? idx[st.t] * u.B + st.hf * kKeys : kKeys * st.c;
   const int last = min(kKeys, (exact ? u.len : u.I) - key0) - 1;
   const int64_t stride = (int64_t)hkv * D;
-  if (exact && kv.page_table != nullptr) {
-    const uint16_t* kh = k + (int64_t)u.h * D;
-    const uint16_t* vh = v + (int64_t)u.h * D;
+  int kkey[C::KL], vkey[C::VL];
 #pragma unroll
-    for (int i = 0; i < C::KL; ++i) {
-      const int f = min(tid + i * C::NT, C::KUN - 1);
-      const int key = min(f / C::KU, last);
-      const int64_t row = kv.row(u.b, u.tok_start, key0 + key);
-      pf.k[i] = *reinterpret_cast<const uint4*>(kh + row * stride + (f % C::KU) * 8);
-    }
+  for (int i = 0; i < C::KL; ++i) kkey[i] = min(min(tid + i * C::NT, C::KUN - 1) / C::KU, last);
+#pragma unroll
+  for (int i = 0; i < C::VL; ++i) vkey[i] = min(2 * (min(tid + i * C::NT, C::VPN - 1) % PAIRS), last);
+  int64_t krow[C::KL], vrow0[C::VL], vrow1[C::VL];
+  if (exact && kv.page_table != nullptr) {
+#pragma unroll
+    for (int i = 0; i < C::KL; ++i) krow[i] = kv.row(u.b, u.tok_start, key0 + kkey[i]);
 #pragma unroll
     for (int i = 0; i < C::VL; ++i) {
-      const int s = min(tid + i * C::NT, C::VPN - 1);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int key = min(2 * (s / C::KU) + c, last);
-        const int64_t row = kv.row(u.b, u.tok_start, key0 + key);
-        pf.v[i][c] = *reinterpret_cast<const uint4*>(vh + row * stride + (s % C::KU) * 8);
-      }
+      vrow0[i] = kv.row(u.b, u.tok_start, key0 + vkey[i]);
+      vrow1[i] = kv.row(u.b, u.tok_start, key0 + min(vkey[i] + 1, last));
     }
   } else {
     const int64_t row0 = exact ? (int64_t)u.tok_start + key0 : (int64_t)u.pool_base + key0;
-    const uint16_t* kh = (exact ? k : kb16) + row0 * stride + (int64_t)u.h * D;
-    const uint16_t* vh = (exact ? v : vb16) + row0 * stride + (int64_t)u.h * D;
 #pragma unroll
-    for (int i = 0; i < C::KL; ++i) {
-      const int f = min(tid + i * C::NT, C::KUN - 1);
-      const int key = min(f / C::KU, last);
-      pf.k[i] = *reinterpret_cast<const uint4*>(kh + key * stride + (f % C::KU) * 8);
-    }
+    for (int i = 0; i < C::KL; ++i) krow[i] = row0 + kkey[i];
 #pragma unroll
     for (int i = 0; i < C::VL; ++i) {
-      const int s = min(tid + i * C::NT, C::VPN - 1);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int key = min(2 * (s / C::KU) + c, last);
-        pf.v[i][c] = *reinterpret_cast<const uint4*>(vh + key * stride + (s % C::KU) * 8);
-      }
+      vrow0[i] = row0 + vkey[i];
+      vrow1[i] = row0 + min(vkey[i] + 1, last);
     }
+  }
+  const uint16_t* kh = (exact ? k : kb16) + (int64_t)u.h * D;
+  const uint16_t* vh = (exact ? v : vb16) + (int64_t)u.h * D;
+#pragma unroll
+  for (int i = 0; i < C::KL; ++i) {
+    const int f = min(tid + i * C::NT, C::KUN - 1);
+    pf.k[i] = *reinterpret_cast<const u32x4_t*>(kh + krow[i] * stride + (f % C::KU) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < C::VL; ++i) {
+    const int un = min(tid + i * C::NT, C::VPN - 1) / PAIRS;
+    pf.v0[i] = *reinterpret_cast<const u32x4_t*>(vh + vrow0[i] * stride + un * 8);
+    pf.v1[i] = *reinterpret_cast<const u32x4_t*>(vh + vrow1[i] * stride + un * 8);
   }
 }
 
@@ -240,16 +242,17 @@ __device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, uint16
     const int f = tid + i * C::NT;
     if (C::KUN % C::NT != 0 && f >= C::KUN) break;
     const int key = f / C::KU, un = f % C::KU;
-    *reinterpret_cast<uint4*>(Ks + key * C::KLD + un * 8) = pf.k[i];
+    *reinterpret_cast<u32x4_t*>(Ks + key * C::KLD + un * 8) = pf.k[i];
   }
 #pragma unroll
   for (int i = 0; i < C::VL; ++i) {
     const int s = tid + i * C::NT;
     if (C::VPN % C::NT != 0 && s >= C::VPN) break;
-    const int a = s / C::KU, un = s % C::KU;
+    // key pairs run fastest across lanes: the 4-byte transposing writes of a
+    // wave then fall in distinct banks (with 16 dims fastest they collide)
+    const int a = s % (kKeys / 2), un = s / (kKeys / 2);
     const int col = kperm(2 * a);  // even; the pair stays adjacent
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&pf.v[i][0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&pf.v[i][1]);
+    const u32x4_t w0 = pf.v0[i], w1 = pf.v1[i];
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
       const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
