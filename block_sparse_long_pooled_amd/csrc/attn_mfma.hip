@@ -76,13 +76,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// One step of the unit's sequence.
+// One step of the unit's sequence.  Every field is the same in all lanes of
+// the workgroup; `uniform` moves them to scalar registers, so branches on
+// them are scalar and reading the block index needs no vector load (which
+// would also make the next step's prefetch wait).
 struct Step {
   int kind;  // StepKind
   int t;     // exact: CSR position
   int hf;    // exact: 64-key half of the block
   int c;     // correction: chunk of 64 pooled blocks
+  int J;     // exact: block index idx[t]
 };
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ void uniform(Step& st) {
+  st.kind = uni(st.kind);
+  st.t = uni(st.t);
+  st.hf = uni(st.hf);
+  st.c = uni(st.c);
+  st.J = uni(st.J);
+}
 
 struct UnitCtx {
   int b, h, I, len, tok_start, pool_base, B, beg, end;
@@ -90,16 +104,16 @@ struct UnitCtx {
 
 // todo bits of correction chunk c (blocks 64c .. 64c+63, valid J <= I-1).
 __device__ __forceinline__ uint64_t chunk_todo(const uint32_t* selbits, int c, int I) {
-  uint64_t bits = 0;
+  uint32_t w2[2] = {0u, 0u};
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
     const int J0 = 64 * c + 32 * w;
     const int nv = min(max(I - J0, 0), 32);
     if (nv == 0) continue;
     const uint32_t m = nv >= 32 ? 0xffffffffu : ((1u << nv) - 1u);
-    bits |= (uint64_t)(~selbits[2 * c + w] & m) << (32 * w);
+    w2[w] = (uint32_t)uni((int)(~selbits[2 * c + w] & m));
   }
-  return bits;
+  return (uint64_t)w2[0] | ((uint64_t)w2[1] << 32);
 }
 
 __device__ __forceinline__ void find_chunk(Step& st, const uint32_t* selbits, int I) {
@@ -118,8 +132,8 @@ __device__ __forceinline__ void advance(Step& st, const UnitCtx& u, const int32_
         --st.t;
       }
       if (st.t < u.beg) break;
-      const int key0 = idx[st.t] * u.B + st.hf * kKeys;
-      if (key0 < u.len) return;  // skip halves past the end of a short last block
+      st.J = uni(idx[st.t]);
+      if (st.J * u.B + st.hf * kKeys < u.len) return;  // skip halves past a short last block
     }
     st.kind = kCorr;
     st.c = -1;
@@ -136,9 +150,10 @@ __device__ __forceinline__ void advance(Step& st, const UnitCtx& u, const int32_
 
 __device__ __forceinline__ Step first_step(const UnitCtx& u, const int32_t* idx,
                                            const uint32_t* selbits, int correction) {
-  Step st{kExact, u.end - 1, -1, 0};
+  Step st{kExact, u.end - 1, -1, 0, 0};
   if (u.end > u.beg) {
     st.hf = 0;
+    st.J = uni(idx[st.t]);
     return st;  // the last selected block always starts inside the request
   }
   st.kind = kCorr;
@@ -171,33 +186,102 @@ struct Prefetch {
   u32x4_t v1[AttnCfg<D, NW, RT>::VL];  // key 2a + 1
 };
 
-// Global -> registers for one step.  Exact steps read tokens key0.. of the
-// request (through the page table when K/V are paged); correction steps read
-// bf16 pooled rows.  Keys past the step's end (the short last block, the
-// last correction chunk) re-read the last valid row: their scores are masked,
-// so only finiteness matters, and the loads need no branch.  Row indices are
-// resolved first and every load is issued from one place, so the values stay
-// in registers while they are in flight.
+// Per-thread byte offsets of the 16-byte pieces this thread fetches, relative
+// to the first row of a step (K/V rows and pooled rows share the [row, Hkv, D]
+// layout); fixed for the whole unit.
 template <int D, int NW, int RT>
-__device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf, const Step& st,
-                                           const UnitCtx& u, const KVDesc& kv, int hkv,
-                                           const uint16_t* k, const uint16_t* v,
-                                           const uint16_t* kb16, const uint16_t* vb16,
-                                           const int32_t* idx) {
+struct FetchOffsets {
+  uint32_t k[AttnCfg<D, NW, RT>::KL];
+  uint32_t v0[AttnCfg<D, NW, RT>::VL];
+  uint32_t v1[AttnCfg<D, NW, RT>::VL];
+};
+
+template <int D, int NW, int RT>
+__device__ __forceinline__ FetchOffsets<D, NW, RT> fetch_offsets(int hkv) {
   using C = AttnCfg<D, NW, RT>;
   constexpr int PAIRS = kKeys / 2;
   const int tid = threadIdx.x;
+  const uint32_t row_bytes = (uint32_t)hkv * D * 2;
+  FetchOffsets<D, NW, RT> o;
+#pragma unroll
+  for (int i = 0; i < C::KL; ++i) {
+    const int f = min(tid + i * C::NT, C::KUN - 1);
+    o.k[i] = (uint32_t)(f / C::KU) * row_bytes + (uint32_t)(f % C::KU) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < C::VL; ++i) {
+    const int s = min(tid + i * C::NT, C::VPN - 1);
+    const uint32_t unit = (uint32_t)(s / PAIRS) * 16;
+    o.v0[i] = (uint32_t)(2 * (s % PAIRS)) * row_bytes + unit;
+    o.v1[i] = (uint32_t)(2 * (s % PAIRS) + 1) * row_bytes + unit;
+  }
+  return o;
+}
+
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)uni((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)uni((int)(uint32_t)(x >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// Global -> registers for one step.  Exact steps read tokens key0.. of the
+// request (through the page table when K/V are paged); correction steps read
+// bf16 pooled rows.  When the step's rows are consecutive in memory
+// (contiguous K/V, pages of at least 64 tokens, pooled rows) the loads are
+// raw buffer loads from one scalar descriptor plus the fixed per-thread
+// offsets; the descriptor ends after the step's last valid key, so keys past
+// the end (the short last block, the last correction chunk) read as zero.
+// With smaller pages every key's row is resolved on its own and keys past the
+// end re-read the last valid row.  Either way those keys' scores are masked.
+template <int D, int NW, int RT>
+__device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
+                                           const FetchOffsets<D, NW, RT>& off, const Step& st,
+                                           const UnitCtx& u, const KVDesc& kv, int hkv,
+                                           const uint16_t* k, const uint16_t* v,
+                                           const uint16_t* kb16, const uint16_t* vb16) {
+  using C = AttnCfg<D, NW, RT>;
+  constexpr int PAIRS = kKeys / 2;
+  constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
   const bool exact = st.kind == kExact;
-  const int key0 = exact ? idx[st.t] * u.B + st.hf * kKeys : kKeys * st.c;
+  const int key0 = exact ? st.J * u.B + st.hf * kKeys : kKeys * st.c;
   const int last = min(kKeys, (exact ? u.len : u.I) - key0) - 1;
+  const bool paged = exact && kv.page_table != nullptr;
   const int64_t stride = (int64_t)hkv * D;
+  if (!paged || kv.page_shift >= 6) {
+    int64_t row0;
+    if (!exact) {
+      row0 = (int64_t)u.pool_base + key0;
+    } else if (paged) {
+      const int phys = uni(kv.page_table[(int64_t)u.b * kv.max_pages + (key0 >> kv.page_shift)]);
+      row0 = ((int64_t)phys << kv.page_shift) | (int64_t)(key0 & ((1 << kv.page_shift) - 1));
+    } else {
+      row0 = (int64_t)u.tok_start + key0;
+    }
+    const int64_t e0 = row0 * stride + (int64_t)u.h * D;
+    const int nrec = uni(last * (int)(stride * 2) + D * 2);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)uniform_ptr((exact ? k : kb16) + e0), (short)0, nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)uniform_ptr((exact ? v : vb16) + e0), (short)0, nrec, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < C::KL; ++i)
+      pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)off.k[i], 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::VL; ++i) {
+      pf.v0[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off.v0[i], 0, 0);
+      pf.v1[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off.v1[i], 0, 0);
+    }
+    return;
+  }
+  const int tid = threadIdx.x;
   int kkey[C::KL], vkey[C::VL];
 #pragma unroll
   for (int i = 0; i < C::KL; ++i) kkey[i] = min(min(tid + i * C::NT, C::KUN - 1) / C::KU, last);
 #pragma unroll
   for (int i = 0; i < C::VL; ++i) vkey[i] = min(2 * (min(tid + i * C::NT, C::VPN - 1) % PAIRS), last);
   int64_t krow[C::KL], vrow0[C::VL], vrow1[C::VL];
-  if (exact && kv.page_table != nullptr) {
+  if (paged) {
 #pragma unroll
     for (int i = 0; i < C::KL; ++i) krow[i] = kv.row(u.b, u.tok_start, key0 + kkey[i]);
 #pragma unroll
@@ -458,15 +542,21 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
   }
   const float bias = __log2f((float)p.B);  // corrected blocks are full blocks
 
+  const FetchOffsets<D, NW, RT> foff = fetch_offsets<D, NW, RT>(p.hkv);
   Prefetch<D, NW, RT> pf;
   Step cur = first_step(u, idx, selbits, correction);
   if (cur.kind != kDone) {
-    fetch_step<D, NW, RT>(pf, cur, u, kv, p.hkv, k, v, kb16, vb16, idx);
+    fetch_step<D, NW, RT>(pf, foff, cur, u, kv, p.hkv, k, v, kb16, vb16);
     store_step<D, NW, RT>(pf, Ks[0], Vt[0]);
   }
+  uniform(cur);
+  // the query rows and the first step have arrived; saying so here keeps the
+  // compiler from waiting on every outstanding load at the top of the loop
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   Step nxt = cur;
   if (cur.kind != kDone) advance(nxt, u, idx, selbits, correction);
-  if (nxt.kind != kDone) fetch_step<D, NW, RT>(pf, nxt, u, kv, p.hkv, k, v, kb16, vb16, idx);
+  uniform(nxt);
+  if (nxt.kind != kDone) fetch_step<D, NW, RT>(pf, foff, nxt, u, kv, p.hkv, k, v, kb16, vb16);
   __syncthreads();
   int buf = 0;
   while (cur.kind != kDone) {
@@ -474,9 +564,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
       int mode, key0 = 0;
       uint64_t todo = 0;
       if (cur.kind == kExact) {
-        const int J = idx[cur.t];
-        key0 = J * p.B + cur.hf * kKeys;
-        mode = J == I ? kDiag : kPlain;
+        key0 = cur.J * p.B + cur.hf * kKeys;
+        mode = cur.J == I ? kDiag : kPlain;
       } else {
         mode = kCorrMode;
         todo = chunk_todo(selbits, cur.c, I);
@@ -489,7 +578,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
     cur = nxt;
     if (nxt.kind != kDone) {
       advance(nxt, u, idx, selbits, correction);
-      if (nxt.kind != kDone) fetch_step<D, NW, RT>(pf, nxt, u, kv, p.hkv, k, v, kb16, vb16, idx);
+      uniform(nxt);
+      if (nxt.kind != kDone) fetch_step<D, NW, RT>(pf, foff, nxt, u, kv, p.hkv, k, v, kb16, vb16);
     }
     buf ^= 1;
   }
