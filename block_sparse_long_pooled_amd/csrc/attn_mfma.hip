@@ -16,10 +16,11 @@
 // selected blocks from the CSR list walked backwards (B/64 steps each), then
 // the correction chunks of 64 pooled blocks that hold at least one block of
 // todo = valid & ~selected (valid = J <= I-1, fully visible to the tile).
-// Every thread derives the same sequence, so no step needs a vote.  Step n+1
-// is fetched from global memory into registers while step n is multiplied
-// out of LDS; the registers are then written to the other LDS buffer, and one
-// barrier per step publishes it.
+// Every thread derives the same sequence, so no step needs a vote.  After
+// the step's barrier each wave writes the prefetched step n+1 into the other
+// LDS buffer, issues the global loads of step n+2 into registers and then
+// multiplies step n, so the loads have a whole step to arrive and the LDS
+// writes of one wave overlap the matrix work of the others.
 //
 // MFMA layout.  Per wave S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32
 // keys x 16 dims of K from LDS, B = the wave's 32 query rows from
@@ -86,6 +87,7 @@ struct Step {
   int hf;    // exact: 64-key half of the block
   int c;     // correction: chunk of 64 pooled blocks
   int J;     // exact: block index idx[t]
+  int Jn;    // exact: idx[t-1], loaded one block ahead so no step waits on it
 };
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -121,19 +123,23 @@ __device__ __forceinline__ void find_chunk(Step& st, const uint32_t* selbits, in
   st.kind = 64 * st.c < I ? kCorr : kDone;
 }
 
-// First step, or the step after `st`.  Identical in every thread.
+// The step after `st`; identical in every thread.  Exact steps run over the
+// selected blocks backwards, B/64 halves each, skipping a second half that
+// lies past the end of a short last block; then come the correction chunks.
+// idx[t-1] is loaded at every exact step and first used one step later, so
+// no step waits for it.
 __device__ __forceinline__ void advance(Step& st, const UnitCtx& u, const int32_t* idx,
                                         const uint32_t* selbits, int correction) {
-  const int halves = u.B / kKeys;
   if (st.kind == kExact) {
-    for (;;) {
-      if (++st.hf == halves) {
-        st.hf = 0;
-        --st.t;
-      }
-      if (st.t < u.beg) break;
-      st.J = uni(idx[st.t]);
-      if (st.J * u.B + st.hf * kKeys < u.len) return;  // skip halves past a short last block
+    ++st.hf;
+    if (st.hf == u.B / kKeys || st.J * u.B + st.hf * kKeys >= u.len) {
+      st.hf = 0;
+      --st.t;
+      st.J = st.Jn;
+    }
+    if (st.t >= u.beg) {
+      st.Jn = idx[max(st.t - 1, u.beg)];
+      return;
     }
     st.kind = kCorr;
     st.c = -1;
@@ -150,11 +156,12 @@ __device__ __forceinline__ void advance(Step& st, const UnitCtx& u, const int32_
 
 __device__ __forceinline__ Step first_step(const UnitCtx& u, const int32_t* idx,
                                            const uint32_t* selbits, int correction) {
-  Step st{kExact, u.end - 1, -1, 0, 0};
+  Step st{kExact, u.end - 1, 0, 0, 0, 0};
   if (u.end > u.beg) {
-    st.hf = 0;
-    st.J = uni(idx[st.t]);
-    return st;  // the last selected block always starts inside the request
+    // the last selected block always starts inside the request
+    st.J = idx[st.t];
+    st.Jn = idx[max(st.t - 1, u.beg)];
+    return st;
   }
   st.kind = kCorr;
   st.c = -1;
@@ -557,9 +564,22 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
   if (cur.kind != kDone) advance(nxt, u, idx, selbits, correction);
   uniform(nxt);
   if (nxt.kind != kDone) fetch_step<D, NW, RT>(pf, foff, nxt, u, kv, p.hkv, k, v, kb16, vb16);
-  __syncthreads();
   int buf = 0;
+  // Per step: barrier (step n is in LDS, the other buffer is free), write the
+  // prefetched step n+1 to the other buffer, issue the loads of step n+2,
+  // multiply step n.  A wave that has written its share starts computing
+  // while the others still write.
   while (cur.kind != kDone) {
+    __syncthreads();
+    // advance first: its scalar index loads were issued a block earlier, and
+    // no LDS write is in flight yet for their wait to cover
+    Step nn = nxt;
+    if (nn.kind != kDone) {
+      advance(nn, u, idx, selbits, correction);
+      uniform(nn);
+    }
+    if (nxt.kind != kDone) store_step<D, NW, RT>(pf, Ks[buf ^ 1], Vt[buf ^ 1]);
+    if (nn.kind != kDone) fetch_step<D, NW, RT>(pf, foff, nn, u, kv, p.hkv, k, v, kb16, vb16);
     if (wave_active) {
       int mode, key0 = 0;
       uint64_t todo = 0;
@@ -573,14 +593,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
       compute_step<D, NW, RT>(Ks[buf], Vt[buf], qf, oacc, m_run, l_run, c, mode, key0, s.len,
                               qpos, todo, bias);
     }
-    if (nxt.kind != kDone) store_step<D, NW, RT>(pf, Ks[buf ^ 1], Vt[buf ^ 1]);
-    __syncthreads();
     cur = nxt;
-    if (nxt.kind != kDone) {
-      advance(nxt, u, idx, selbits, correction);
-      uniform(nxt);
-      if (nxt.kind != kDone) fetch_step<D, NW, RT>(pf, foff, nxt, u, kv, p.hkv, k, v, kb16, vb16);
-    }
+    nxt = nn;
     buf ^= 1;
   }
 
