@@ -207,11 +207,12 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
   bslp::AttnArgs a{q, k, v, kbar, vbar, cu, idx, out, lse, workspace,
                    problem->softmax_scale * problem->q_scale, problem->k_scale,
                    problem->v_scale, sa.correction};
-  // bf16 runs on the matrix cores; float32 keeps exact fp32 arithmetic on the
-  // vector ALUs.
-  const hipError_t e = problem->dtype == BSLP_BF16
-                           ? bslp::launch_attn_mfma_bf16(plan, kv, a, (hipStream_t)stream)
-                           : bslp::launch_attn_valu(plan, kv, problem->dtype, a,
+  // bf16 and fp8 run on the matrix cores; float32 keeps exact fp32
+  // arithmetic on the vector ALUs.
+  const hipError_t e = problem->dtype == BSLP_F32
+                           ? bslp::launch_attn_valu(plan, kv, problem->dtype, a,
+                                                    (hipStream_t)stream)
+                           : bslp::launch_attn_mfma(plan, kv, problem->dtype, a,
                                                     (hipStream_t)stream);
   return hip_result(e, "bslp_sparse_prefill_attn");
 }

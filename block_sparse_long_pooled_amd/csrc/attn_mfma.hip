@@ -1,5 +1,6 @@
 // Stage 3 on the matrix cores: block-sparse causal online-softmax attention
-// with mean correction and PackGQA rows, bf16 inputs ("FlashPrefill V2",
+// with mean correction and PackGQA rows, bf16 or fp8 (e4m3) inputs
+// ("FlashPrefill V2",
 // Sec. 3.1 last sentence, Sec. 3.2 / Fig. 3 correction path, PackGQA, CSR
 // and paged-KV paragraphs).  Written for gfx950 wave64 MFMA.
 //
@@ -14,8 +15,12 @@
 //
 // Pipeline.  The unit's work is a uniform sequence of 64-key steps: the
 // selected blocks from the CSR list walked backwards (B/64 steps each), then
-// the correction chunks of 64 pooled blocks that hold at least one block of
+// the correction chunks of 32 pooled blocks that hold at least one block of
 // todo = valid & ~selected (valid = J <= I-1, fully visible to the tile).
+// A correction step's 64 keys are the 32 pooled means as bf16 pairs hi + lo
+// (the float32 mean to within 2^-18 of itself): keys 0-31 hold hi, keys
+// 32-63 lo, and the two score halves are added before the softmax, so the
+// pooled logits carry no bf16 rounding.
 // Every thread derives the same sequence, so no step needs a vote.  After
 // the step's barrier each wave writes the prefetched step n+1 into the other
 // LDS buffer, issues the global loads of step n+2 into registers and then
@@ -49,7 +54,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16 bytes, kept
 
 namespace {
 
-constexpr int kKeys = 64;  // keys per pipeline step
+constexpr int kKeys = 64;      // keys per pipeline step
+constexpr int kCorrRows = 32;  // pooled blocks per correction step (hi + lo keys)
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum StepKind : int { kExact = 0, kCorr = 1, kDone = 2 };
@@ -77,6 +83,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Eight OCP e4m3 codes (two little-endian words) widened to eight bf16.  Every
+// e4m3 value is exact in bf16, and its bf16 bits are the top half of the
+// float32 bits, so a byte permute packs each pair without rounding.
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+  r[1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
+  r[3] = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
+  return r;
+}
+
 // One step of the unit's sequence.  Every field is the same in all lanes of
 // the workgroup; `uniform` moves them to scalar registers, so branches on
 // them are scalar and reading the block index needs no vector load (which
@@ -85,7 +107,7 @@ struct Step {
   int kind;  // StepKind
   int t;     // exact: CSR position
   int hf;    // exact: 64-key half of the block
-  int c;     // correction: chunk of 64 pooled blocks
+  int c;     // correction: chunk of 32 pooled blocks
   int J;     // exact: block index idx[t]
   int Jn;    // exact: idx[t-1], loaded one block ahead so no step waits on it
 };
@@ -104,23 +126,17 @@ struct UnitCtx {
   int b, h, I, len, tok_start, pool_base, B, beg, end;
 };
 
-// todo bits of correction chunk c (blocks 64c .. 64c+63, valid J <= I-1).
+// todo bits of correction chunk c (blocks 32c .. 32c+31, valid J <= I-1).
 __device__ __forceinline__ uint64_t chunk_todo(const uint32_t* selbits, int c, int I) {
-  uint32_t w2[2] = {0u, 0u};
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    const int J0 = 64 * c + 32 * w;
-    const int nv = min(max(I - J0, 0), 32);
-    if (nv == 0) continue;
-    const uint32_t m = nv >= 32 ? 0xffffffffu : ((1u << nv) - 1u);
-    w2[w] = (uint32_t)uni((int)(~selbits[2 * c + w] & m));
-  }
-  return (uint64_t)w2[0] | ((uint64_t)w2[1] << 32);
+  const int nv = min(max(I - kCorrRows * c, 0), kCorrRows);
+  if (nv == 0) return 0;
+  const uint32_t m = nv >= 32 ? 0xffffffffu : ((1u << nv) - 1u);
+  return (uint32_t)uni((int)(~selbits[c] & m));
 }
 
 __device__ __forceinline__ void find_chunk(Step& st, const uint32_t* selbits, int I) {
-  while (64 * st.c < I && chunk_todo(selbits, st.c, I) == 0) ++st.c;
-  st.kind = 64 * st.c < I ? kCorr : kDone;
+  while (kCorrRows * st.c < I && chunk_todo(selbits, st.c, I) == 0) ++st.c;
+  st.kind = kCorrRows * st.c < I ? kCorr : kDone;
 }
 
 // The step after `st`; identical in every thread.  Exact steps run over the
@@ -193,9 +209,10 @@ struct Prefetch {
   u32x4_t v1[AttnCfg<D, NW, RT>::VL];  // key 2a + 1
 };
 
-// Per-thread byte offsets of the 16-byte pieces this thread fetches, relative
-// to the first row of a step (K/V rows and pooled rows share the [row, Hkv, D]
-// layout); fixed for the whole unit.
+// Per-thread byte offsets of the 8-element pieces this thread fetches,
+// relative to the first row of a step (K/V rows and pooled rows share the
+// [row, Hkv, D] layout), for 2-byte (bf16) and 1-byte (e4m3) elements; fixed
+// for the whole unit.
 template <int D, int NW, int RT>
 struct FetchOffsets {
   uint32_t k[AttnCfg<D, NW, RT>::KL];
@@ -204,21 +221,21 @@ struct FetchOffsets {
 };
 
 template <int D, int NW, int RT>
-__device__ __forceinline__ FetchOffsets<D, NW, RT> fetch_offsets(int hkv) {
+__device__ __forceinline__ FetchOffsets<D, NW, RT> fetch_offsets(int hkv, int esize) {
   using C = AttnCfg<D, NW, RT>;
   constexpr int PAIRS = kKeys / 2;
   const int tid = threadIdx.x;
-  const uint32_t row_bytes = (uint32_t)hkv * D * 2;
+  const uint32_t row_bytes = (uint32_t)hkv * D * esize;
   FetchOffsets<D, NW, RT> o;
 #pragma unroll
   for (int i = 0; i < C::KL; ++i) {
     const int f = min(tid + i * C::NT, C::KUN - 1);
-    o.k[i] = (uint32_t)(f / C::KU) * row_bytes + (uint32_t)(f % C::KU) * 16;
+    o.k[i] = (uint32_t)(f / C::KU) * row_bytes + (uint32_t)(f % C::KU) * 8 * esize;
   }
 #pragma unroll
   for (int i = 0; i < C::VL; ++i) {
     const int s = min(tid + i * C::NT, C::VPN - 1);
-    const uint32_t unit = (uint32_t)(s / PAIRS) * 16;
+    const uint32_t unit = (uint32_t)(s / PAIRS) * 8 * esize;
     o.v0[i] = (uint32_t)(2 * (s % PAIRS)) * row_bytes + unit;
     o.v1[i] = (uint32_t)(2 * (s % PAIRS) + 1) * row_bytes + unit;
   }
@@ -232,55 +249,113 @@ __device__ __forceinline__ const char* uniform_ptr(const void* p) {
   return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
 }
 
-// Global -> registers for one step.  Exact steps read tokens key0.. of the
-// request (through the page table when K/V are paged); correction steps read
-// bf16 pooled rows.  When the step's rows are consecutive in memory
-// (contiguous K/V, pages of at least 64 tokens, pooled rows) the loads are
-// raw buffer loads from one scalar descriptor plus the fixed per-thread
-// offsets; the descriptor ends after the step's last valid key, so keys past
-// the end (the short last block, the last correction chunk) read as zero.
-// With smaller pages every key's row is resolved on its own and keys past the
-// end re-read the last valid row.  Either way those keys' scores are masked.
+// Offsets of the K pieces of a correction step: key r < 32 is the hi row of
+// pooled block r, key 32 + r its lo row, from the [pooled row, {hi, lo}, Hkv,
+// D] bf16 layout.
 template <int D, int NW, int RT>
+struct CorrOffsets {
+  uint32_t k[AttnCfg<D, NW, RT>::KL];
+};
+
+template <int D, int NW, int RT>
+__device__ __forceinline__ CorrOffsets<D, NW, RT> corr_offsets(int hkv) {
+  using C = AttnCfg<D, NW, RT>;
+  const int tid = threadIdx.x;
+  const uint32_t row_bytes = (uint32_t)hkv * D * 2;
+  CorrOffsets<D, NW, RT> o;
+#pragma unroll
+  for (int i = 0; i < C::KL; ++i) {
+    const int f = min(tid + i * C::NT, C::KUN - 1);
+    const int key = f / C::KU;
+    o.k[i] = (uint32_t)(2 * (key % kCorrRows) + key / kCorrRows) * row_bytes +
+             (uint32_t)(f % C::KU) * 16;
+  }
+  return o;
+}
+
+// Global -> registers for one step.  Exact steps read tokens key0.. of the
+// request (through the page table when K/V are paged), as bf16 or as e4m3
+// codes (8 bytes per piece, widened when written to LDS); correction steps
+// read the bf16 hi/lo rows of 32 pooled keys and their 32 pooled values.
+// When the step's rows are consecutive in memory (contiguous K/V, pages of at
+// least 64 tokens, pooled rows) the loads are raw buffer loads from one
+// scalar descriptor plus the fixed per-thread offsets; the descriptor ends
+// after the step's last valid row, so rows past it (the short last block, the
+// last correction chunk, the value rows of keys 32-63 of a correction step)
+// read as zero.  With smaller pages every key's row is resolved on its own
+// and keys past the end re-read the last valid row.  Either way those keys'
+// scores are masked.
+template <int DT, int D, int NW, int RT>
 __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
-                                           const FetchOffsets<D, NW, RT>& off, const Step& st,
+                                           const FetchOffsets<D, NW, RT>& off16,
+                                           const FetchOffsets<D, NW, RT>& off8,
+                                           const CorrOffsets<D, NW, RT>& offc, const Step& st,
                                            const UnitCtx& u, const KVDesc& kv, int hkv,
-                                           const uint16_t* k, const uint16_t* v,
-                                           const uint16_t* kb16, const uint16_t* vb16) {
+                                           const void* k, const void* v,
+                                           const uint16_t* kb2, const uint16_t* vb16) {
   using C = AttnCfg<D, NW, RT>;
   constexpr int PAIRS = kKeys / 2;
   constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
   const bool exact = st.kind == kExact;
-  const int key0 = exact ? st.J * u.B + st.hf * kKeys : kKeys * st.c;
-  const int last = min(kKeys, (exact ? u.len : u.I) - key0) - 1;
+  const bool codes = DT == kFP8 && exact;  // 1-byte e4m3 elements
+  const int esize = codes ? 1 : 2;
+  const int key0 = exact ? st.J * u.B + st.hf * kKeys : kCorrRows * st.c;
+  const int last = exact ? min(kKeys, u.len - key0) - 1 : min(kCorrRows, u.I - key0) - 1;
   const bool paged = exact && kv.page_table != nullptr;
   const int64_t stride = (int64_t)hkv * D;
+  const char* ksrc = exact ? static_cast<const char*>(k) : reinterpret_cast<const char*>(kb2);
+  const char* vsrc = exact ? static_cast<const char*>(v) : reinterpret_cast<const char*>(vb16);
   if (!paged || kv.page_shift >= 6) {
-    int64_t row0;
+    int64_t kb0, vb0;
+    int nrec_k, nrec_v;
     if (!exact) {
-      row0 = (int64_t)u.pool_base + key0;
-    } else if (paged) {
-      const int phys = uni(kv.page_table[(int64_t)u.b * kv.max_pages + (key0 >> kv.page_shift)]);
-      row0 = ((int64_t)phys << kv.page_shift) | (int64_t)(key0 & ((1 << kv.page_shift) - 1));
+      const int64_t prow = (int64_t)u.pool_base + key0;
+      kb0 = (prow * 2 * stride + (int64_t)u.h * D) * 2;
+      vb0 = (prow * stride + (int64_t)u.h * D) * 2;
+      nrec_k = ((2 * last + 1) * (int)stride + D) * 2;
+      nrec_v = (last * (int)stride + D) * 2;
     } else {
-      row0 = (int64_t)u.tok_start + key0;
+      int64_t row0;
+      if (paged) {
+        const int phys = uni(kv.page_table[(int64_t)u.b * kv.max_pages + (key0 >> kv.page_shift)]);
+        row0 = ((int64_t)phys << kv.page_shift) | (int64_t)(key0 & ((1 << kv.page_shift) - 1));
+      } else {
+        row0 = (int64_t)u.tok_start + key0;
+      }
+      kb0 = vb0 = (row0 * stride + (int64_t)u.h * D) * esize;
+      nrec_k = nrec_v = (last * (int)stride + D) * esize;
     }
-    const int64_t e0 = row0 * stride + (int64_t)u.h * D;
-    const int nrec = uni(last * (int)(stride * 2) + D * 2);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)uniform_ptr((exact ? k : kb16) + e0), (short)0, nrec, kRsrcWord3);
+        (void*)uniform_ptr(ksrc + kb0), (short)0, uni(nrec_k), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)uniform_ptr((exact ? v : vb16) + e0), (short)0, nrec, kRsrcWord3);
+        (void*)uniform_ptr(vsrc + vb0), (short)0, uni(nrec_v), kRsrcWord3);
+    if (codes) {
 #pragma unroll
-    for (int i = 0; i < C::KL; ++i)
-      pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)off.k[i], 0, 0);
+      for (int i = 0; i < C::KL; ++i) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(rk, (int)off8.k[i], 0, 0);
+        pf.k[i] = u32x4_t{w[0], w[1], 0u, 0u};
+      }
 #pragma unroll
-    for (int i = 0; i < C::VL; ++i) {
-      pf.v0[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off.v0[i], 0, 0);
-      pf.v1[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off.v1[i], 0, 0);
+      for (int i = 0; i < C::VL; ++i) {
+        const auto w0 = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)off8.v0[i], 0, 0);
+        const auto w1 = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)off8.v1[i], 0, 0);
+        pf.v0[i] = u32x4_t{w0[0], w0[1], 0u, 0u};
+        pf.v1[i] = u32x4_t{w1[0], w1[1], 0u, 0u};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::KL; ++i)
+        pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(exact ? off16.k[i] : offc.k[i]),
+                                                        0, 0);
+#pragma unroll
+      for (int i = 0; i < C::VL; ++i) {
+        pf.v0[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off16.v0[i], 0, 0);
+        pf.v1[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off16.v1[i], 0, 0);
+      }
     }
     return;
   }
+  // paged with pages below 64 tokens: exact steps only
   const int tid = threadIdx.x;
   int kkey[C::KL], vkey[C::VL];
 #pragma unroll
@@ -288,44 +363,46 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
 #pragma unroll
   for (int i = 0; i < C::VL; ++i) vkey[i] = min(2 * (min(tid + i * C::NT, C::VPN - 1) % PAIRS), last);
   int64_t krow[C::KL], vrow0[C::VL], vrow1[C::VL];
-  if (paged) {
 #pragma unroll
-    for (int i = 0; i < C::KL; ++i) krow[i] = kv.row(u.b, u.tok_start, key0 + kkey[i]);
+  for (int i = 0; i < C::KL; ++i) krow[i] = kv.row(u.b, u.tok_start, key0 + kkey[i]);
 #pragma unroll
-    for (int i = 0; i < C::VL; ++i) {
-      vrow0[i] = kv.row(u.b, u.tok_start, key0 + vkey[i]);
-      vrow1[i] = kv.row(u.b, u.tok_start, key0 + min(vkey[i] + 1, last));
-    }
-  } else {
-    const int64_t row0 = exact ? (int64_t)u.tok_start + key0 : (int64_t)u.pool_base + key0;
-#pragma unroll
-    for (int i = 0; i < C::KL; ++i) krow[i] = row0 + kkey[i];
-#pragma unroll
-    for (int i = 0; i < C::VL; ++i) {
-      vrow0[i] = row0 + vkey[i];
-      vrow1[i] = row0 + min(vkey[i] + 1, last);
-    }
+  for (int i = 0; i < C::VL; ++i) {
+    vrow0[i] = kv.row(u.b, u.tok_start, key0 + vkey[i]);
+    vrow1[i] = kv.row(u.b, u.tok_start, key0 + min(vkey[i] + 1, last));
   }
-  const uint16_t* kh = (exact ? k : kb16) + (int64_t)u.h * D;
-  const uint16_t* vh = (exact ? v : vb16) + (int64_t)u.h * D;
+  const int64_t hoff = (int64_t)u.h * D;
 #pragma unroll
   for (int i = 0; i < C::KL; ++i) {
     const int f = min(tid + i * C::NT, C::KUN - 1);
-    pf.k[i] = *reinterpret_cast<const u32x4_t*>(kh + krow[i] * stride + (f % C::KU) * 8);
+    const int64_t e = krow[i] * stride + hoff + (f % C::KU) * 8;
+    if (codes) {
+      const uint2 w = *reinterpret_cast<const uint2*>(ksrc + e);
+      pf.k[i] = u32x4_t{w.x, w.y, 0u, 0u};
+    } else {
+      pf.k[i] = *reinterpret_cast<const u32x4_t*>(ksrc + 2 * e);
+    }
   }
 #pragma unroll
   for (int i = 0; i < C::VL; ++i) {
     const int un = min(tid + i * C::NT, C::VPN - 1) / PAIRS;
-    pf.v0[i] = *reinterpret_cast<const u32x4_t*>(vh + vrow0[i] * stride + un * 8);
-    pf.v1[i] = *reinterpret_cast<const u32x4_t*>(vh + vrow1[i] * stride + un * 8);
+    const int64_t e0 = vrow0[i] * stride + hoff + un * 8, e1 = vrow1[i] * stride + hoff + un * 8;
+    if (codes) {
+      const uint2 w0 = *reinterpret_cast<const uint2*>(vsrc + e0);
+      const uint2 w1 = *reinterpret_cast<const uint2*>(vsrc + e1);
+      pf.v0[i] = u32x4_t{w0.x, w0.y, 0u, 0u};
+      pf.v1[i] = u32x4_t{w1.x, w1.y, 0u, 0u};
+    } else {
+      pf.v0[i] = *reinterpret_cast<const u32x4_t*>(vsrc + 2 * e0);
+      pf.v1[i] = *reinterpret_cast<const u32x4_t*>(vsrc + 2 * e1);
+    }
   }
 }
 
 // Registers -> LDS: K row-major, V transposed with permuted key columns; both
 // with padded rows so the 16-byte operand reads of 16 lanes hit distinct banks.
 template <int D, int NW, int RT>
-__device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, uint16_t* Ks,
-                                           uint16_t* Vt) {
+__device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, bool widen,
+                                           uint16_t* Ks, uint16_t* Vt) {
   using C = AttnCfg<D, NW, RT>;
   const int tid = threadIdx.x;
 #pragma unroll
@@ -333,7 +410,8 @@ __device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, uint16
     const int f = tid + i * C::NT;
     if (C::KUN % C::NT != 0 && f >= C::KUN) break;
     const int key = f / C::KU, un = f % C::KU;
-    *reinterpret_cast<u32x4_t*>(Ks + key * C::KLD + un * 8) = pf.k[i];
+    *reinterpret_cast<u32x4_t*>(Ks + key * C::KLD + un * 8) =
+        widen ? e4m3x8_to_bf16x8(pf.k[i][0], pf.k[i][1]) : pf.k[i];
   }
 #pragma unroll
   for (int i = 0; i < C::VL; ++i) {
@@ -343,7 +421,8 @@ __device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, uint16
     // wave then fall in distinct banks (with 16 dims fastest they collide)
     const int a = s % (kKeys / 2), un = s / (kKeys / 2);
     const int col = kperm(2 * a);  // even; the pair stays adjacent
-    const u32x4_t w0 = pf.v0[i], w1 = pf.v1[i];
+    const u32x4_t w0 = widen ? e4m3x8_to_bf16x8(pf.v0[i][0], pf.v0[i][1]) : pf.v0[i];
+    const u32x4_t w1 = widen ? e4m3x8_to_bf16x8(pf.v1[i][0], pf.v1[i][1]) : pf.v1[i];
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
       const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
@@ -391,6 +470,14 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
   // masks: diagonal block (token causality and the request end) or the
   // correction chunk's todo bits; branch-free per element, uniform per step
   if (mode != kPlain) {
+    if (mode == kCorrMode) {
+      // pooled logits: hi keys 0-31 plus lo keys 32-63 (masked below)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[rt][0][r] += sacc[rt][1][r];
+      }
+    }
     uint64_t bits;
     if (mode == kDiag) {
       const int nvis = len - key0;  // >= 1
@@ -468,13 +555,13 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
   }
 }
 
-template <int D, int NW, int RT>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
-    Plan p, KVDesc kv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ kb16,
+template <int DT, int D, int NW, int RT>
+__global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
+    Plan p, KVDesc kv, const void* __restrict__ q, const void* __restrict__ k,
+    const void* __restrict__ v, const uint16_t* __restrict__ kb2,
     const uint16_t* __restrict__ vb16, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ idx, float c, int correction, int units_per_seg,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const int32_t* __restrict__ idx, float c, float out_scale, int correction,
+    int units_per_seg, uint16_t* __restrict__ out, float* __restrict__ lse) {
   using C = AttnCfg<D, NW, RT>;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKeys * C::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VLD];
@@ -517,8 +604,17 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
     const int64_t qoff = ((int64_t)(s.tok_start + qpos[rt]) * p.hq + hqs[rt]) * D;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (valid[rt]) w = *reinterpret_cast<const uint4*>(q + qoff + ks * 16 + half * 8);
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (valid[rt]) {
+        if constexpr (DT == kFP8) {
+          const uint2 cw = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(q) + qoff +
+                                                           ks * 16 + half * 8);
+          w = e4m3x8_to_bf16x8(cw.x, cw.y);
+        } else {
+          w = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(q) + qoff + ks * 16 +
+                                                half * 8);
+        }
+      }
       qf[rt][ks] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
@@ -549,12 +645,14 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
   }
   const float bias = __log2f((float)p.B);  // corrected blocks are full blocks
 
-  const FetchOffsets<D, NW, RT> foff = fetch_offsets<D, NW, RT>(p.hkv);
+  const FetchOffsets<D, NW, RT> off16 = fetch_offsets<D, NW, RT>(p.hkv, 2);
+  const FetchOffsets<D, NW, RT> off8 = fetch_offsets<D, NW, RT>(p.hkv, DT == kFP8 ? 1 : 2);
+  const CorrOffsets<D, NW, RT> offc = corr_offsets<D, NW, RT>(p.hkv);
   Prefetch<D, NW, RT> pf;
   Step cur = first_step(u, idx, selbits, correction);
   if (cur.kind != kDone) {
-    fetch_step<D, NW, RT>(pf, foff, cur, u, kv, p.hkv, k, v, kb16, vb16);
-    store_step<D, NW, RT>(pf, Ks[0], Vt[0]);
+    fetch_step<DT, D, NW, RT>(pf, off16, off8, offc, cur, u, kv, p.hkv, k, v, kb2, vb16);
+    store_step<D, NW, RT>(pf, DT == kFP8 && cur.kind == kExact, Ks[0], Vt[0]);
   }
   uniform(cur);
   // the query rows and the first step have arrived; saying so here keeps the
@@ -563,7 +661,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
   Step nxt = cur;
   if (cur.kind != kDone) advance(nxt, u, idx, selbits, correction);
   uniform(nxt);
-  if (nxt.kind != kDone) fetch_step<D, NW, RT>(pf, foff, nxt, u, kv, p.hkv, k, v, kb16, vb16);
+  if (nxt.kind != kDone) fetch_step<DT, D, NW, RT>(pf, off16, off8, offc, nxt, u, kv, p.hkv, k, v, kb2, vb16);
   int buf = 0;
   // Per step: barrier (step n is in LDS, the other buffer is free), write the
   // prefetched step n+1 to the other buffer, issue the loads of step n+2,
@@ -578,8 +676,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
       advance(nn, u, idx, selbits, correction);
       uniform(nn);
     }
-    if (nxt.kind != kDone) store_step<D, NW, RT>(pf, Ks[buf ^ 1], Vt[buf ^ 1]);
-    if (nn.kind != kDone) fetch_step<D, NW, RT>(pf, foff, nn, u, kv, p.hkv, k, v, kb16, vb16);
+    if (nxt.kind != kDone)
+      store_step<D, NW, RT>(pf, DT == kFP8 && nxt.kind == kExact, Ks[buf ^ 1], Vt[buf ^ 1]);
+    if (nn.kind != kDone) fetch_step<DT, D, NW, RT>(pf, off16, off8, offc, nn, u, kv, p.hkv, k, v, kb2, vb16);
     if (wave_active) {
       int mode, key0 = 0;
       uint64_t todo = 0;
@@ -603,7 +702,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
   for (int rt = 0; rt < RT; ++rt) {
     const float l_tot = halves_sum(l_run[rt]);
     if (!valid[rt]) continue;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? out_scale / l_tot : 0.f;
     const int64_t ooff = ((int64_t)(s.tok_start + qpos[rt]) * p.hq + hqs[rt]) * D;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
@@ -623,31 +722,53 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
   }
 }
 
-// float32 pooled means -> bf16 (round to nearest even) for the correction
-// steps; n8 = number of 8-element groups.
+// float32 pooled means -> bf16 for the correction steps, divided by the
+// per-tensor K / V scales of fp8 inputs so that they share the scale of the
+// e4m3 codes.  Keys become the pair hi = bf16(x), lo = bf16(x - hi) (x - hi is
+// exact in float32, so hi + lo is x to within 2^-18 |x|), stored as
+// [pooled row, {hi, lo}, Hkv, D]; values are rounded once, [pooled row, Hkv,
+// D].  n8 = 8-element groups per tensor, row8 = groups per pooled row.
 __global__ __launch_bounds__(256) void pooled_to_bf16_kernel(const float* __restrict__ kbar,
                                                             const float* __restrict__ vbar,
-                                                            int64_t n8, uint16_t* __restrict__ kb16,
+                                                            int64_t n8, int row8, float k_inv,
+                                                            float v_inv,
+                                                            uint16_t* __restrict__ kb2,
                                                             uint16_t* __restrict__ vb16) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= 2 * n8) return;
   const bool is_v = i >= n8;
   const int64_t j = is_v ? i - n8 : i;
   const float* src = (is_v ? vbar : kbar) + 8 * j;
+  const float sc = is_v ? v_inv : k_inv;
+  float x[8];
   const float4 a = *reinterpret_cast<const float4*>(src);
   const float4 bq = *reinterpret_cast<const float4*>(src + 4);
-  const uint4 w = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
-                             pack_bf16x2(bq.x, bq.y), pack_bf16x2(bq.z, bq.w));
-  *reinterpret_cast<uint4*>((is_v ? vb16 : kb16) + 8 * j) = w;
+  x[0] = a.x * sc; x[1] = a.y * sc; x[2] = a.z * sc; x[3] = a.w * sc;
+  x[4] = bq.x * sc; x[5] = bq.y * sc; x[6] = bq.z * sc; x[7] = bq.w * sc;
+  u32x4_t hi, lo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    const float h0 = __uint_as_float(hi[e] << 16), h1 = __uint_as_float(hi[e] & 0xffff0000u);
+    lo[e] = pack_bf16x2(x[2 * e] - h0, x[2 * e + 1] - h1);
+  }
+  if (is_v) {
+    *reinterpret_cast<u32x4_t*>(vb16 + 8 * j) = hi;
+  } else {
+    const int64_t row = j / row8, col = j % row8;
+    *reinterpret_cast<u32x4_t*>(kb2 + 8 * (row * 2 * row8 + col)) = hi;
+    *reinterpret_cast<u32x4_t*>(kb2 + 8 * (row * 2 * row8 + row8 + col)) = lo;
+  }
 }
 
 size_t attn_workspace_bytes(const Plan& p) {
+  // pooled keys as hi/lo bf16 pairs, pooled values as bf16
   const size_t n = (size_t)p.pooled_rows * p.hkv * p.d;  // elements per pooled tensor
-  return 2 * n * sizeof(uint16_t);
+  return 3 * n * sizeof(uint16_t);
 }
 
-template <int D, int NW, int RT>
-static hipError_t launch_bf16_t(const Plan& p, const KVDesc& kv, const AttnArgs& a,
+template <int DT, int D, int NW, int RT>
+static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs& a,
                                 hipStream_t st) {
   const int rows = AttnCfg<D, NW, RT>::ROWS;
   const int units_per_seg = (p.g * p.B + rows - 1) / rows;
@@ -662,35 +783,38 @@ static hipError_t launch_bf16_t(const Plan& p, const KVDesc& kv, const AttnArgs&
   }
   if (base == 0) return hipSuccess;
   const size_t n = (size_t)p.pooled_rows * p.hkv * p.d;
-  uint16_t* kb16 = reinterpret_cast<uint16_t*>(a.workspace);
-  uint16_t* vb16 = kb16 + n;
+  uint16_t* kb2 = reinterpret_cast<uint16_t*>(a.workspace);
+  uint16_t* vb16 = kb2 + 2 * n;
   if (n > 0) {
     const int64_t n8 = (int64_t)(n / 8);
     hipLaunchKernelGGL(pooled_to_bf16_kernel, dim3((unsigned)((2 * n8 + 255) / 256)), dim3(256),
-                       0, st, a.kbar, a.vbar, n8, kb16, vb16);
+                       0, st, a.kbar, a.vbar, n8, p.hkv * p.d / 8, 1.f / a.k_scale,
+                       1.f / a.v_scale, kb2, vb16);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, RT>), dim3((unsigned)base), dim3(NW * 64), 0, st,
-                     pl, kv, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)kb16, (const uint16_t*)vb16, a.cu, a.idx,
-                     a.lscale * 1.4426950408889634f, a.correction, units_per_seg,
-                     (uint16_t*)a.out, a.lse);
+  // logits of the codes: softmax_scale * q_scale * k_scale, in units of log2
+  const float c = (float)((double)a.lscale * (double)a.k_scale * 1.4426950408889634);
+  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT>), dim3((unsigned)base), dim3(NW * 64), 0,
+                     st, pl, kv, a.q, a.k, a.v, (const uint16_t*)kb2, (const uint16_t*)vb16, a.cu,
+                     a.idx, c, a.v_scale, a.correction, units_per_seg, (uint16_t*)a.out, a.lse);
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_bf16_d(const Plan& p, const KVDesc& kv, const AttnArgs& a,
+template <int DT, int D>
+static hipError_t launch_mfma_d(const Plan& p, const KVDesc& kv, const AttnArgs& a,
                                 hipStream_t st) {
   const int rows = p.g * p.B;
-  if (rows >= 256) return launch_bf16_t<D, 8, 1>(p, kv, a, st);
-  if (rows >= 128) return launch_bf16_t<D, 4, 1>(p, kv, a, st);
-  return launch_bf16_t<D, 2, 1>(p, kv, a, st);
+  if (rows >= 256) return launch_mfma_t<DT, D, 8, 1>(p, kv, a, st);
+  if (rows >= 128) return launch_mfma_t<DT, D, 4, 1>(p, kv, a, st);
+  return launch_mfma_t<DT, D, 2, 1>(p, kv, a, st);
 }
 
-hipError_t launch_attn_mfma_bf16(const Plan& p, const KVDesc& kv, const AttnArgs& a,
-                                 hipStream_t st) {
-  return p.d == 128 ? launch_bf16_d<128>(p, kv, a, st) : launch_bf16_d<64>(p, kv, a, st);
+hipError_t launch_attn_mfma(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
+                            hipStream_t st) {
+  if (dtype == kFP8)
+    return p.d == 128 ? launch_mfma_d<kFP8, 128>(p, kv, a, st) : launch_mfma_d<kFP8, 64>(p, kv, a, st);
+  return p.d == 128 ? launch_mfma_d<kBF16, 128>(p, kv, a, st) : launch_mfma_d<kBF16, 64>(p, kv, a, st);
 }
 
 }  // namespace bslp

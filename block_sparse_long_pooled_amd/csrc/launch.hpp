@@ -43,7 +43,8 @@ hipError_t launch_attn_valu(const Plan& p, const KVDesc& kv, int dtype, const At
 // Device scratch the attention launch needs (bf16 copies of the pooled means).
 size_t attn_workspace_bytes(const Plan& p);
 
-hipError_t launch_attn_mfma_bf16(const Plan& p, const KVDesc& kv, const AttnArgs& a,
-                                 hipStream_t st);
+// bf16 and fp8 inputs on the matrix cores (fp8 codes widen exactly to bf16).
+hipError_t launch_attn_mfma(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
+                            hipStream_t st);
 
 }  // namespace bslp

@@ -163,8 +163,8 @@ bslp_status bslp_select_blocks(const bslp_problem* problem, const bslp_select_pa
  * problem.  Only params->mean_correction is read.
  * workspace: device scratch of at least bslp_sizes.workspace_bytes bytes,
  * 16-byte aligned, owned by the caller; its contents on entry do not matter
- * and are overwritten (the call keeps lower-precision copies of kbar / vbar
- * there).  Calls that overlap in time must not share a workspace. */
+ * and are overwritten (the call keeps bf16 copies of kbar, as hi + lo pairs,
+ * and of vbar there).  Calls that overlap in time must not share a workspace. */
 bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
                                      const bslp_select_params* params, const void* q,
                                      const void* k, const void* v, const float* kbar,
