@@ -6,6 +6,11 @@ already resident in HBM: pooling + block scores, selection, and block-sparse
 attention with mean correction.  Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+                    [--copy-calibration]
+
+--copy-calibration ends the run with three plain device copies of 1 GiB, the
+known-size reference that scales the FETCH_SIZE / WRITE_SIZE counters of a
+rocprofv3 --pmc run of this same command into bytes.
 
 Workload (default): 64K-token bf16 GQA prefill, Hq=32, Hkv=8, d=128, B=128,
 alpha=0.05, sink 1 / window 2 / recent 1 blocks, mean correction on, inputs
@@ -40,6 +45,35 @@ CONFIGS = {
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+# arithmetic type of the attention contraction per input type: e4m3 inputs
+# are widened exactly to bf16 and run on the bf16 matrix cores
+COMPUTE_DTYPE = {"f32": "f32", "bf16": "bf16", "fp8": "bf16"}
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_long_pooled_amd", "csrc", "attn_mfma.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter summary of
+    this workload, or None when there is none or the attention kernel source
+    has changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"attn_mfma_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    with open(ATTN_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("kernel_source_sha256") != digest:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def dense_flops(w) -> float:
@@ -142,6 +176,7 @@ def main():
     ap.add_argument("--config", default="64k-bf16", choices=sorted(CONFIGS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the operator has no "
@@ -201,7 +236,8 @@ def main():
     f_dense = dense_flops(w)
     attn_ms = float(ms_stage[2])
     achieved = f_eff / (attn_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
+    cdt = COMPUTE_DTYPE[w.dtype]
+    peak = PEAK_TFLOPS[cdt]
 
     # block-score stage algorithmic bytes: Q read once, K and V read once for
     # pooling, pooled K/V written, score rows written
@@ -223,11 +259,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": cdt,
         "data": "synthetic (seeded planted-block generator)",
         "config": {
             "workload": w.name, "seqlens": list(w.seqlens), "hq": w.hq, "hkv": w.hkv,
-            "head_dim": w.d, "block": w.block, "alpha": w.alpha, "sink_blocks": w.sink,
+            "input_dtype": w.dtype, "head_dim": w.d, "block": w.block, "alpha": w.alpha, "sink_blocks": w.sink,
             "window_blocks": w.window, "recent_blocks": w.recent,
             "mean_correction": bool(w.correction), "page_size": w.page_size,
             "density": round(density, 5),
@@ -242,13 +278,20 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
             "effective_flops": f_eff,
         },
         "block_scores_hbm": {"bytes": s1_bytes, "gbs": s1_bytes / (ms_stage[0] * 1e-3) / 1e9,
                              "frac_of_8TBs": s1_bytes / (ms_stage[0] * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "input_gen_s": round(t_gen, 2),
     }
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = 1 << 30
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(res), flush=True)
