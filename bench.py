@@ -177,6 +177,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--dense-reps", type=int, default=3,
+                    help="timed calls of the dense causal path (0 skips it)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the operator has no "
@@ -285,6 +287,23 @@ def main():
                              "frac_of_8TBs": s1_bytes / (ms_stage[0] * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "input_gen_s": round(t_gen, 2),
     }
+    if args.dense_reps > 0:
+        # the in-framework dense baseline: same kernel, every causal block
+        dout = torch.empty_like(bufs.out)
+        dlse = torch.empty_like(bufs.lse)
+        bslp.dense_prefill_attn(prob, q, k, v, dout, dlse, sp)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.dense_reps):
+            bslp.dense_prefill_attn(prob, q, k, v, dout, dlse, sp)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / args.dense_reps
+        dense_tf = f_dense / (dense_ms * 1e-3) / 1e12
+        res["dense_attention"] = {"ms": dense_ms, "tflops": dense_tf, "frac": dense_tf / peak,
+                                  "sparse_layer_speedup": dense_ms / ms_step}
+        del dout, dlse
     if args.copy_calibration:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

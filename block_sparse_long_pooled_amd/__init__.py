@@ -73,7 +73,8 @@ class Sizes(ctypes.Structure):
 
 
 EXPORTS = ("bslp_get_sizes", "bslp_block_scores", "bslp_select_blocks",
-           "bslp_sparse_prefill_attn", "bslp_status_string", "bslp_last_error")
+           "bslp_sparse_prefill_attn", "bslp_dense_prefill_attn", "bslp_status_string",
+           "bslp_last_error")
 
 _lib = None
 
@@ -94,8 +95,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bslp_select_blocks.argtypes = [P(Problem), P(SelectParams), vp, vp, vp, vp, vp]
     lib.bslp_sparse_prefill_attn.argtypes = [P(Problem), P(SelectParams), vp, vp, vp, vp, vp,
                                              vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.bslp_dense_prefill_attn.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp]
     for name in ("bslp_get_sizes", "bslp_block_scores", "bslp_select_blocks",
-                 "bslp_sparse_prefill_attn"):
+                 "bslp_sparse_prefill_attn", "bslp_dense_prefill_attn"):
         getattr(lib, name).restype = ctypes.c_int
     lib.bslp_status_string.argtypes = [ctypes.c_int]
     lib.bslp_status_string.restype = ctypes.c_char_p
@@ -182,6 +184,13 @@ def sparse_prefill_attn(problem, params, q, k, v, kbar, vbar, cu, idx, out, lse=
                                                    _stream(stream)))
 
 
+def dense_prefill_attn(problem, q, k, v, out, lse=None, stream=None):
+    """Dense causal attention over every key j <= i (no index stage)."""
+    _check(load_library().bslp_dense_prefill_attn(ctypes.byref(problem), _ptr(q), _ptr(k),
+                                                  _ptr(v), _ptr(out), _ptr(lse),
+                                                  _stream(stream)))
+
+
 class Buffers:
     """Device buffers of one prefill call, allocated with torch."""
 
@@ -215,5 +224,6 @@ def prefill(problem, params, q, k, v, bufs: Buffers | None = None, stream=None) 
 
 
 __all__ = ["BF16", "F32", "FP8_E4M3", "BslpError", "Buffers", "EXPORTS", "LIB_PATH", "Problem",
-           "SelectParams", "Sizes", "block_scores", "get_sizes", "load_library", "make_params",
+           "SelectParams", "Sizes", "block_scores", "dense_prefill_attn", "get_sizes",
+           "load_library", "make_params",
            "make_problem", "prefill", "select_blocks", "sparse_prefill_attn"]

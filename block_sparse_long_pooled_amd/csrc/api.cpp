@@ -206,7 +206,7 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
     return fail(BSLP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   bslp::AttnArgs a{q, k, v, kbar, vbar, cu, idx, out, lse, workspace,
                    problem->softmax_scale * problem->q_scale, problem->k_scale,
-                   problem->v_scale, sa.correction};
+                   problem->v_scale, sa.correction, 0};
   // bf16 and fp8 run on the matrix cores; float32 keeps exact fp32
   // arithmetic on the vector ALUs.
   const hipError_t e = problem->dtype == BSLP_F32
@@ -215,6 +215,25 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
                            : bslp::launch_attn_mfma(plan, kv, problem->dtype, a,
                                                     (hipStream_t)stream);
   return hip_result(e, "bslp_sparse_prefill_attn");
+}
+
+bslp_status bslp_dense_prefill_attn(const bslp_problem* problem, const void* q, const void* k,
+                                    const void* v, void* out, float* lse, void* stream) {
+  bslp::Plan plan;
+  bslp::KVDesc kv;
+  bslp_status st = build_plan(problem, &plan, &kv);
+  if (st != BSLP_OK) return st;
+  if (plan.total_tokens == 0) return BSLP_OK;
+  if (!q || !k || !v || !out) return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  bslp::AttnArgs a{q, k, v, nullptr, nullptr, nullptr, nullptr, out, lse, nullptr,
+                   problem->softmax_scale * problem->q_scale, problem->k_scale,
+                   problem->v_scale, 0, 1};
+  const hipError_t e = problem->dtype == BSLP_F32
+                           ? bslp::launch_attn_valu(plan, kv, problem->dtype, a,
+                                                    (hipStream_t)stream)
+                           : bslp::launch_attn_mfma(plan, kv, problem->dtype, a,
+                                                    (hipStream_t)stream);
+  return hip_result(e, "bslp_dense_prefill_attn");
 }
 
 const char* bslp_status_string(bslp_status status) {

@@ -124,7 +124,13 @@ __device__ __forceinline__ void uniform(Step& st) {
 
 struct UnitCtx {
   int b, h, I, len, tok_start, pool_base, B, beg, end;
+  int dense;  // blocks are J = t for t in [0, I]: no index list
 };
+
+// Block index at CSR position t (the position itself on the dense path).
+__device__ __forceinline__ int block_at(const int32_t* idx, int t, const UnitCtx& u) {
+  return u.dense ? t : idx[t];
+}
 
 // todo bits of correction chunk c (blocks 32c .. 32c+31, valid J <= I-1).
 __device__ __forceinline__ uint64_t chunk_todo(const uint32_t* selbits, int c, int I) {
@@ -154,7 +160,7 @@ __device__ __forceinline__ void advance(Step& st, const UnitCtx& u, const int32_
       st.J = st.Jn;
     }
     if (st.t >= u.beg) {
-      st.Jn = idx[max(st.t - 1, u.beg)];
+      st.Jn = block_at(idx, max(st.t - 1, u.beg), u);
       return;
     }
     st.kind = kCorr;
@@ -175,8 +181,8 @@ __device__ __forceinline__ Step first_step(const UnitCtx& u, const int32_t* idx,
   Step st{kExact, u.end - 1, 0, 0, 0, 0};
   if (u.end > u.beg) {
     // the last selected block always starts inside the request
-    st.J = idx[st.t];
-    st.Jn = idx[max(st.t - 1, u.beg)];
+    st.J = block_at(idx, st.t, u);
+    st.Jn = block_at(idx, max(st.t - 1, u.beg), u);
     return st;
   }
   st.kind = kCorr;
@@ -560,7 +566,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     Plan p, KVDesc kv, const void* __restrict__ q, const void* __restrict__ k,
     const void* __restrict__ v, const uint16_t* __restrict__ kb2,
     const uint16_t* __restrict__ vb16, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ idx, float c, float out_scale, int correction,
+    const int32_t* __restrict__ idx, float c, float out_scale, int correction, int dense,
     int units_per_seg, uint16_t* __restrict__ out, float* __restrict__ lse) {
   using C = AttnCfg<D, NW, RT>;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKeys * C::KLD];
@@ -587,7 +593,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   const int64_t seg = (int64_t)s.seg_base + (int64_t)h * s.nblk + I;
   const int nb = min(p.B, s.len - I * p.B);
   const int R = p.g * nb;
-  UnitCtx u{b, h, I, s.len, s.tok_start, s.pool_base, p.B, cu[seg], cu[seg + 1]};
+  UnitCtx u{b, h, I, s.len, s.tok_start, s.pool_base, p.B, dense ? 0 : cu[seg],
+            dense ? I + 1 : cu[seg + 1], dense};
 
   // ---- this lane's query rows (B operands of Q K^T), one per row tile
   const int row0 = mt * C::ROWS + wave * RT * 32;
@@ -785,7 +792,7 @@ static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs&
   const size_t n = (size_t)p.pooled_rows * p.hkv * p.d;
   uint16_t* kb2 = reinterpret_cast<uint16_t*>(a.workspace);
   uint16_t* vb16 = kb2 + 2 * n;
-  if (n > 0) {
+  if (n > 0 && a.correction && !a.dense) {
     const int64_t n8 = (int64_t)(n / 8);
     hipLaunchKernelGGL(pooled_to_bf16_kernel, dim3((unsigned)((2 * n8 + 255) / 256)), dim3(256),
                        0, st, a.kbar, a.vbar, n8, p.hkv * p.d / 8, 1.f / a.k_scale,
@@ -797,7 +804,8 @@ static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs&
   const float c = (float)((double)a.lscale * (double)a.k_scale * 1.4426950408889634);
   hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT>), dim3((unsigned)base), dim3(NW * 64), 0,
                      st, pl, kv, a.q, a.k, a.v, (const uint16_t*)kb2, (const uint16_t*)vb16, a.cu,
-                     a.idx, c, a.v_scale, a.correction, units_per_seg, (uint16_t*)a.out, a.lse);
+                     a.idx, c, a.v_scale, a.correction && !a.dense, a.dense, units_per_seg,
+                     (uint16_t*)a.out, a.lse);
   return hipGetLastError();
 }
 

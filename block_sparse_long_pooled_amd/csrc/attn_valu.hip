@@ -66,7 +66,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
     const typename Elem<DT>::T* __restrict__ k, const typename Elem<DT>::T* __restrict__ v,
     const float* __restrict__ kbar, const float* __restrict__ vbar,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ idx, float lscale, float k_scale,
-    float v_scale, int correction, int units_per_seg, void* __restrict__ out,
+    float v_scale, int correction, int dense, int units_per_seg, void* __restrict__ out,
     float* __restrict__ lse) {
   __shared__ float Ks[32][D];
   __shared__ float Vs[32][D];
@@ -106,9 +106,10 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
   st.m = -INFINITY;
   st.l = 0.f;
 
-  const int beg = cu[seg], end = cu[seg + 1];
-  for (int t = end - 1; t >= beg; --t) {  // CSR walked backwards
-    const int J = idx[t];
+  // CSR walked backwards; the dense path walks every block J <= I
+  const int beg = dense ? 0 : cu[seg], end = dense ? I + 1 : cu[seg + 1];
+  for (int t = end - 1; t >= beg; --t) {
+    const int J = dense ? t : idx[t];
     const int j0 = J * p.B;
     const int cnt = min(p.B, s.len - j0);
     for (int sub = 0; sub < cnt; sub += 32) {
@@ -194,7 +195,8 @@ static hipError_t launch_attn_valu_t(const Plan& p, const KVDesc& kv, const Attn
   if (units == 0) return hipSuccess;
   hipLaunchKernelGGL((attn_valu_kernel<DT, D>), dim3((unsigned)units), dim3(64), 0, st, p, kv,
                      (const T*)a.q, (const T*)a.k, (const T*)a.v, a.kbar, a.vbar, a.cu, a.idx,
-                     a.lscale, a.k_scale, a.v_scale, a.correction, units_per_seg, a.out, a.lse);
+                     a.lscale, a.k_scale, a.v_scale, a.correction && !a.dense, a.dense, units_per_seg,
+                     a.out, a.lse);
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ struct AttnArgs {
   float k_scale;  // 1 unless fp8
   float v_scale;
   int correction;
+  int dense;  // walk every causal block J <= I (cu, idx, kbar, vbar unused)
 };
 
 hipError_t launch_stage1(const Plan& p, const KVDesc& kv, int dtype, const void* q, const void* k,

@@ -172,6 +172,20 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
                                      void* out, float* lse, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* Dense causal prefill attention on the same kernels, with no index stage:
+ * every row attends to all keys j <= i of its request, as a
+ * FlashAttention-style dense baseline against which the block-sparse path's
+ * speedup is measured ("FlashPrefill V2", Sec. 4 comparisons with dense
+ * FlashAttention; its kernel-speed figures).
+ *
+ * q, k, v, page table, out and lse as in bslp_sparse_prefill_attn (same
+ * layouts, dtypes and scales); no pooled means, index or workspace are read.
+ * The result equals bslp_sparse_prefill_attn's with every causal block
+ * selected and mean correction off, bit for bit: the same blocks are walked
+ * in the same order.  Errors: as bslp_sparse_prefill_attn. */
+bslp_status bslp_dense_prefill_attn(const bslp_problem* problem, const void* q, const void* k,
+                                    const void* v, void* out, float* lse, void* stream);
+
 /* Static text for a status code. */
 const char* bslp_status_string(bslp_status status);
 /* Detail of the calling thread's last failing call ("" if none). */

@@ -165,3 +165,14 @@ def test_attention_workspace_validated_before_launch():
         p, params, t, t, t, t, t, t, t, t, t,
         workspace=FakeTensor(nbytes=need, ptr=0x1008), stream=0))
     assert st == 1 and "aligned" in d
+
+
+def test_dense_attention_validated_before_launch():
+    t = FakeTensor()
+    st, d = _status(lambda: bslp.dense_prefill_attn(_problem(), t, None, t, t, stream=0))
+    assert st == 1 and "NULL" in d
+    st, _ = _status(lambda: bslp.dense_prefill_attn(_problem(head_dim=80), t, t, t, t,
+                                                    stream=0))
+    assert st == 2
+    # nothing to do for an empty problem, so NULL pointers are fine
+    bslp.dense_prefill_attn(_problem(seqlens=[0]), None, None, None, None, stream=0)
