@@ -31,8 +31,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import (FP8_128K, GQA_BF16_16K, PAGED_VARLEN, SWEEP_BF16_64K,  # noqa: E402
-                       TINY_F32, make_inputs)
+from workloads import (FP8_128K, GQA_BF16_16K, PAGED_VARLEN, SHARD_BF16_16K,  # noqa: E402
+                       SWEEP_BF16_64K, TINY_F32, make_inputs)
 
 METRIC = "sparse prefill ms/layer + dense-equiv TFLOP/s at 64K/128K (MFMA % of peak)"
 CONFIGS = {
@@ -40,6 +40,7 @@ CONFIGS = {
     "128k-fp8": FP8_128K,
     "16k-bf16": GQA_BF16_16K,
     "paged-varlen": PAGED_VARLEN,
+    "16k-tp8-shard": SHARD_BF16_16K,
     "tiny-f32": TINY_F32,
 }
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
@@ -177,6 +178,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--kv-splits", type=int, default=0,
+                    help="attention KV splits: 0 automatic, 1 none, 2..16 forced")
     ap.add_argument("--dense-reps", type=int, default=3,
                     help="timed calls of the dense causal path (0 skips it)")
     args = ap.parse_args()
@@ -198,7 +201,8 @@ def main():
     table = torch.from_numpy(inp.table).to(dev) if inp.table is not None else None
     prob = bslp.make_problem(w.dtype, w.hq, w.hkv, w.d, w.block, w.seqlens,
                              softmax_scale=w.scale, q_scale=inp.q_scale, k_scale=inp.k_scale,
-                             v_scale=inp.v_scale, page_table=table, page_size=w.page_size)
+                             v_scale=inp.v_scale, page_table=table, page_size=w.page_size,
+                             kv_splits=args.kv_splits)
     params = bslp.make_params(w.alpha, w.sink, w.window, w.recent, w.correction)
     bufs = bslp.Buffers(prob)
     stream = torch.cuda.current_stream()
@@ -268,6 +272,7 @@ def main():
             "input_dtype": w.dtype, "head_dim": w.d, "block": w.block, "alpha": w.alpha, "sink_blocks": w.sink,
             "window_blocks": w.window, "recent_blocks": w.recent,
             "mean_correction": bool(w.correction), "page_size": w.page_size,
+            "kv_splits": args.kv_splits,
             "density": round(density, 5),
         },
         "ms_per_layer": ms_step,

@@ -49,6 +49,7 @@ class Problem(ctypes.Structure):
         ("page_table", ctypes.c_void_p),
         ("page_size", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32),
+        ("kv_splits", ctypes.c_int32),
     ]
 
 
@@ -114,9 +115,11 @@ def _check(status: int):
 
 def make_problem(dtype: str, hq: int, hkv: int, head_dim: int, block_size: int, seqlens,
                  softmax_scale: float | None = None, q_scale: float = 1.0, k_scale: float = 1.0,
-                 v_scale: float = 1.0, page_table=None, page_size: int = 0) -> Problem:
+                 v_scale: float = 1.0, page_table=None, page_size: int = 0,
+                 kv_splits: int = 0) -> Problem:
     """Fills the problem descriptor.  `page_table` is a device int32 tensor
-    [num_seqs, max_pages] (or None for contiguous K/V)."""
+    [num_seqs, max_pages] (or None for contiguous K/V); `kv_splits` 0 lets the
+    library choose the attention's KV splits, 1 turns them off."""
     lens = (ctypes.c_int32 * len(seqlens))(*[int(x) for x in seqlens])
     p = Problem()
     p.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
@@ -125,6 +128,7 @@ def make_problem(dtype: str, hq: int, hkv: int, head_dim: int, block_size: int, 
     p.softmax_scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(head_dim)
     p.q_scale, p.k_scale, p.v_scale = q_scale, k_scale, v_scale
     p.num_seqs = len(seqlens)
+    p.kv_splits = kv_splits
     p.seqlens = lens
     p._keep = [lens, page_table]
     if page_table is not None:

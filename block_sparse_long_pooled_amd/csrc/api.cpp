@@ -53,6 +53,8 @@ bslp_status build_plan(const bslp_problem* pr, bslp::Plan* plan, bslp::KVDesc* k
     if (pr->max_pages_per_seq < 1)
       return fail(BSLP_ERR_INVALID_ARG, "max_pages_per_seq must be >= 1");
   }
+  if (pr->kv_splits < 0 || pr->kv_splits > bslp::kMaxSplits)
+    return fail(BSLP_ERR_INVALID_ARG, "kv_splits must be in 0 .. 16");
 
   *plan = bslp::Plan{};
   plan->num_seqs = pr->num_seqs;
@@ -142,7 +144,8 @@ bslp_status bslp_get_sizes(const bslp_problem* problem, bslp_sizes* out) {
   out->pooled_rows = plan.pooled_rows;
   out->score_elems = plan.score_elems;
   out->num_segments = plan.num_segments;
-  out->workspace_bytes = (int64_t)bslp::attn_workspace_bytes(plan);
+  out->workspace_bytes = (int64_t)bslp::attn_workspace_bytes(
+      plan, bslp::attn_splits(plan, problem->dtype, problem->kv_splits));
   return BSLP_OK;
 }
 
@@ -196,7 +199,8 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
   if (plan.total_tokens == 0) return BSLP_OK;
   if (!q || !k || !v || !kbar || !vbar || !cu || !idx || !out)
     return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
-  const size_t need = bslp::attn_workspace_bytes(plan);
+  const int splits = bslp::attn_splits(plan, problem->dtype, problem->kv_splits);
+  const size_t need = bslp::attn_workspace_bytes(plan, splits);
   if (workspace_bytes < need)
     return fail(BSLP_ERR_INVALID_ARG, "workspace_bytes " + std::to_string(workspace_bytes) +
                                           " is below the " + std::to_string(need) +
@@ -206,7 +210,7 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
     return fail(BSLP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   bslp::AttnArgs a{q, k, v, kbar, vbar, cu, idx, out, lse, workspace,
                    problem->softmax_scale * problem->q_scale, problem->k_scale,
-                   problem->v_scale, sa.correction, 0};
+                   problem->v_scale, sa.correction, 0, splits};
   // bf16 and fp8 run on the matrix cores; float32 keeps exact fp32
   // arithmetic on the vector ALUs.
   const hipError_t e = problem->dtype == BSLP_F32
@@ -227,7 +231,7 @@ bslp_status bslp_dense_prefill_attn(const bslp_problem* problem, const void* q, 
   if (!q || !k || !v || !out) return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
   bslp::AttnArgs a{q, k, v, nullptr, nullptr, nullptr, nullptr, out, lse, nullptr,
                    problem->softmax_scale * problem->q_scale, problem->k_scale,
-                   problem->v_scale, 0, 1};
+                   problem->v_scale, 0, 1, 1};
   const hipError_t e = problem->dtype == BSLP_F32
                            ? bslp::launch_attn_valu(plan, kv, problem->dtype, a,
                                                     (hipStream_t)stream)

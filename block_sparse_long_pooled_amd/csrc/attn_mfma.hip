@@ -43,6 +43,8 @@
 // raised only when a step exceeds it by more than 8 (so p < 2^8), which makes
 // the output rescale rare.  Correction terms enter as s*c + log2|B_J| with
 // unselected or invisible columns at -inf.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -123,9 +125,21 @@ __device__ __forceinline__ void uniform(Step& st) {
 }
 
 struct UnitCtx {
-  int b, h, I, len, tok_start, pool_base, B, beg, end;
-  int dense;  // blocks are J = t for t in [0, I]: no index list
+  int b, h, I, len, tok_start, pool_base, B;
+  int beg, end;  // the unit's share of the CSR positions of its segment
+  int dense;     // blocks are J = t for t in [0, I]: no index list
+  int c0, cstep; // correction chunks c0, c0 + cstep, ... belong to the unit
 };
+
+// KV splits a segment actually uses, at most `splits`: one per 24 steps of
+// estimated work (its selected blocks in 64-key halves plus an upper bound on
+// its correction chunks), so light segments stay whole and write no partial
+// result.  The attention and the merge kernel evaluate it alike.
+__device__ __forceinline__ int segment_splits(int n_sel, int I, int B, int correction,
+                                              int splits) {
+  const int steps = n_sel * (B / 64) + (correction && I > 0 ? (I + 31) / 32 : 0);
+  return max(1, min(splits, steps / 24));
+}
 
 // Block index at CSR position t (the position itself on the dense path).
 __device__ __forceinline__ int block_at(const int32_t* idx, int t, const UnitCtx& u) {
@@ -140,8 +154,8 @@ __device__ __forceinline__ uint64_t chunk_todo(const uint32_t* selbits, int c, i
   return (uint32_t)uni((int)(~selbits[c] & m));
 }
 
-__device__ __forceinline__ void find_chunk(Step& st, const uint32_t* selbits, int I) {
-  while (kCorrRows * st.c < I && chunk_todo(selbits, st.c, I) == 0) ++st.c;
+__device__ __forceinline__ void find_chunk(Step& st, const uint32_t* selbits, int I, int cstep) {
+  while (kCorrRows * st.c < I && chunk_todo(selbits, st.c, I) == 0) st.c += cstep;
   st.kind = kCorrRows * st.c < I ? kCorr : kDone;
 }
 
@@ -164,15 +178,15 @@ __device__ __forceinline__ void advance(Step& st, const UnitCtx& u, const int32_
       return;
     }
     st.kind = kCorr;
-    st.c = -1;
+    st.c = u.c0 - u.cstep;
   }
   if (st.kind == kCorr) {
     if (!correction || u.I == 0) {
       st.kind = kDone;
       return;
     }
-    ++st.c;
-    find_chunk(st, selbits, u.I);
+    st.c += u.cstep;
+    find_chunk(st, selbits, u.I, u.cstep);
   }
 }
 
@@ -186,7 +200,7 @@ __device__ __forceinline__ Step first_step(const UnitCtx& u, const int32_t* idx,
     return st;
   }
   st.kind = kCorr;
-  st.c = -1;
+  st.c = u.c0 - u.cstep;
   advance(st, u, idx, selbits, correction);
   return st;
 }
@@ -567,34 +581,33 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const void* __restrict__ v, const uint16_t* __restrict__ kb2,
     const uint16_t* __restrict__ vb16, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ idx, float c, float out_scale, int correction, int dense,
-    int units_per_seg, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int units_per_seg, int splits, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ items,
+    int* __restrict__ queue) {
   using C = AttnCfg<D, NW, RT>;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKeys * C::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VLD];
   __shared__ uint32_t selbits[kMaxBlocksPerSeq / 32];
+  __shared__ int next_item;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
 
-  // ---- unit -> (request, tile I, row block mt, KV head h)
-  const int64_t unit = blockIdx.x;
-  int pos = 0;
-  while (pos + 1 < p.num_seqs && p.seq[p.order[pos + 1]].unit_base <= unit) ++pos;
-  const int b = p.order[pos];
+  // One work unit: (segment (b, h, I), row block mt, KV split sp).
+  auto run_unit = [&](int b, int I, int h, int mt, int sp) __attribute__((always_inline)) {
   const SeqInfo s = p.seq[b];
-  const int64_t local = unit - s.unit_base;
-  const int per_I = p.hkv * units_per_seg;
-  const int I = s.nblk - 1 - (int)(local / per_I);
-  const int rem = (int)(local % per_I);
-  const int mt = rem / p.hkv;
-  const int h = rem % p.hkv;
   const int64_t seg = (int64_t)s.seg_base + (int64_t)h * s.nblk + I;
   const int nb = min(p.B, s.len - I * p.B);
   const int R = p.g * nb;
-  UnitCtx u{b, h, I, s.len, s.tok_start, s.pool_base, p.B, dense ? 0 : cu[seg],
-            dense ? I + 1 : cu[seg + 1], dense};
+  // split sp of the segment's ns takes a contiguous share of the CSR
+  // positions, balanced by count, and every ns-th correction chunk
+  const int beg0 = dense ? 0 : cu[seg], n_sel = (dense ? I + 1 : cu[seg + 1]) - beg0;
+  const int ns = splits == 1 ? 1 : segment_splits(n_sel, I, p.B, correction, splits);
+  UnitCtx u{b, h, I, s.len, s.tok_start, s.pool_base, p.B,
+            beg0 + (int)((int64_t)sp * n_sel / ns),
+            beg0 + (int)((int64_t)(sp + 1) * n_sel / ns), dense, sp, ns};
 
   // ---- this lane's query rows (B operands of Q K^T), one per row tile
   const int row0 = mt * C::ROWS + wave * RT * 32;
@@ -631,8 +644,10 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const int nwords = (I + 31) >> 5;
     for (int w = tid; w < nwords; w += C::NT) selbits[w] = 0u;
     __syncthreads();
-    for (int t = u.beg + tid; t < u.end; t += C::NT) {
-      const int J = idx[t];
+    // every selected block of the segment, not only this split's share: the
+    // others are attended exactly by the other splits
+    for (int t = beg0 + tid; t < beg0 + n_sel; t += C::NT) {
+      const int J = block_at(idx, t, u);
       if (J < I) atomicOr(&selbits[J >> 5], 1u << (J & 31));
     }
     __syncthreads();
@@ -704,13 +719,33 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     buf ^= 1;
   }
 
-  // ---- epilogue: l over all keys of the row = both lane halves
+  // ---- epilogue: l over all keys of the row = both lane halves.  A split
+  // unit leaves its partial result (O normalised by its own l, the log2
+  // reference m and l) for the merge kernel.
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float l_tot = halves_sum(l_run[rt]);
     if (!valid[rt]) continue;
     const float inv = l_tot > 0.f ? out_scale / l_tot : 0.f;
-    const int64_t ooff = ((int64_t)(s.tok_start + qpos[rt]) * p.hq + hqs[rt]) * D;
+    const int64_t orow = (int64_t)(s.tok_start + qpos[rt]) * p.hq + hqs[rt];
+    if (ns > 1) {
+      const int64_t prow = (int64_t)sp * p.total_tokens * p.hq + orow;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = dt * 32 + g4 * 8 + half * 4;
+          *reinterpret_cast<float4*>(part_o + prow * D + d) =
+              make_float4(oacc[rt][dt][4 * g4] * inv, oacc[rt][dt][4 * g4 + 1] * inv,
+                          oacc[rt][dt][4 * g4 + 2] * inv, oacc[rt][dt][4 * g4 + 3] * inv);
+        }
+      }
+      if (half == 0)
+        *reinterpret_cast<float2*>(part_ml + 2 * prow) =
+            make_float2(l_tot > 0.f ? m_run[rt] : -INFINITY, l_tot);
+      continue;
+    }
+    const int64_t ooff = orow * D;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
@@ -726,6 +761,148 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     if (lse && half == 0)
       lse[(int64_t)hqs[rt] * p.total_tokens + s.tok_start + qpos[rt]] =
           l_tot > 0.f ? m_run[rt] * kLn2 + __logf(l_tot) : -INFINITY;
+  }
+  };
+
+  if (items == nullptr) {
+    // one workgroup per unit, enumerated heaviest first: longest request
+    // first, tiles in descending I, then row block, KV head innermost
+    const int64_t unit = blockIdx.x;
+    int pos = 0;
+    while (pos + 1 < p.num_seqs && p.seq[p.order[pos + 1]].unit_base <= unit) ++pos;
+    const int b = p.order[pos];
+    const int64_t local = unit - p.seq[b].unit_base;
+    const int per_I = p.hkv * units_per_seg;
+    const int rem = (int)(local % per_I);
+    run_unit(b, p.seq[b].nblk - 1 - (int)(local / per_I), rem % p.hkv, rem / p.hkv, 0);
+    return;
+  }
+  // split launch: persistent workgroups take items from the list the
+  // preparation kernel wrote (heaviest segments first) until it is empty
+  const int n_items = queue[1];
+  for (;;) {
+    if (tid == 0) next_item = atomicAdd(&queue[0], 1);
+    __syncthreads();
+    const int it = next_item;
+    __syncthreads();  // every wave has read it (and left the last unit's LDS)
+    if (it >= n_items) break;
+    const int code = items[it];
+    const int64_t seg = code >> 8;
+    int b = 0;
+    while (b + 1 < p.num_seqs && p.seq[b + 1].seg_base <= seg) ++b;
+    const int local = (int)(seg - p.seq[b].seg_base);
+    run_unit(b, local % p.seq[b].nblk, local / p.seq[b].nblk, (code >> 4) & 15, code & 15);
+  }
+
+}
+
+// Merge of the KV splits of the rows of every split segment: with M =
+// max_u m_u and weights w_u = l_u 2^(m_u - M), O = sum_u w_u O_u / sum_u w_u
+// and LSE = M ln 2 + ln sum_u w_u (the split-combine of "FlashPrefill V2",
+// Sec. 3.3 KV splitting).  One workgroup per segment (b, h, I); segments that
+// were not split wrote their rows directly and are skipped.
+template <int D>
+__global__ __launch_bounds__(256) void merge_splits_kernel(Plan p, const int32_t* __restrict__ cu,
+                                                           const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           int splits, int correction,
+                                                           uint16_t* __restrict__ out,
+                                                           float* __restrict__ lse) {
+  const int64_t seg = blockIdx.x;
+  const int b = seq_of_segment(p, seg);
+  const SeqInfo s = p.seq[b];
+  const int local = (int)(seg - s.seg_base);
+  const int h = local / s.nblk, I = local % s.nblk;
+  const int ns = segment_splits(cu[seg + 1] - cu[seg], I, p.B, correction, splits);
+  if (ns == 1) return;
+  const int nb = min(p.B, s.len - I * p.B);
+  const int64_t prows = p.total_tokens * p.hq;  // rows of one split's partials
+  for (int i = threadIdx.x; i < p.g * nb * (D / 4); i += 256) {
+    const int r = i / (D / 4), d = (i % (D / 4)) * 4;
+    const int64_t tok = s.tok_start + I * p.B + r / p.g;
+    const int hq = h * p.g + r % p.g;
+    const int64_t row = tok * p.hq + hq;
+    float M = -INFINITY;
+    for (int u = 0; u < ns; ++u) M = fmaxf(M, part_ml[2 * (u * prows + row)]);
+    float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    if (M != -INFINITY) {
+      for (int u = 0; u < ns; ++u) {
+        const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * (u * prows + row));
+        if (ml.x == -INFINITY) continue;
+        const float w = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
+        const float4 o = *reinterpret_cast<const float4*>(part_o + (u * prows + row) * D + d);
+        L += w;
+        o0 = fmaf(w, o.x, o0);
+        o1 = fmaf(w, o.y, o1);
+        o2 = fmaf(w, o.z, o2);
+        o3 = fmaf(w, o.w, o3);
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    *reinterpret_cast<uint2*>(out + row * D + d) =
+        make_uint2(pack_bf16x2(o0 * inv, o1 * inv), pack_bf16x2(o2 * inv, o3 * inv));
+    if (lse && d == 0) lse[(int64_t)hq * p.total_tokens + tok] = L > 0.f ? M * kLn2 + __logf(L) : -INFINITY;
+  }
+}
+
+// Work list of a split launch ("FlashPrefill V2", Sec. 3.3: splits balanced by
+// selected count, heaviest work first): one workgroup walks the segments in
+// the order of the unsplit launch (longest request first, tiles in
+// descending I, KV head innermost), gives each its split count from its
+// selected count and writes one item (segment << 8 | row block << 4 | split)
+// per (row block, split), with a block-wide prefix sum for the offsets.
+// queue[0] is the next item to take, queue[1] the number of items.
+__global__ __launch_bounds__(1024) void split_items_kernel(Plan p, const int32_t* __restrict__ cu,
+                                                           int splits, int correction,
+                                                           int units_per_seg,
+                                                           int32_t* __restrict__ items,
+                                                           int* __restrict__ queue) {
+  __shared__ int wsum[16];
+  __shared__ int carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < p.num_segments; base += 1024) {
+    const int64_t q = base + tid;
+    int n = 0, seg = 0, I = 0;
+    if (q < p.num_segments) {
+      // q-th segment in launch order
+      int i = 0;
+      int64_t qb = 0;
+      while (qb + (int64_t)p.seq[p.order[i]].nblk * p.hkv <= q) {
+        qb += (int64_t)p.seq[p.order[i]].nblk * p.hkv;
+        ++i;
+      }
+      const SeqInfo& si = p.seq[p.order[i]];
+      const int local = (int)(q - qb);
+      I = si.nblk - 1 - local / p.hkv;
+      seg = si.seg_base + (local % p.hkv) * si.nblk + I;
+      n = segment_splits(cu[seg + 1] - cu[seg], I, p.B, correction, splits) * units_per_seg;
+    }
+    // block-wide exclusive prefix sum of n
+    int x = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = carry_s;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int off = before + x - n;
+    if (n > 0) {
+      const int ns = n / units_per_seg;
+      for (int t = 0; t < n; ++t)
+        items[off + t] = (seg << 8) | ((t / ns) << 4) | (t % ns);
+    }
+    __syncthreads();
+    if (tid == 1023) carry_s = off + n;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    queue[0] = 0;
+    queue[1] = carry_s;
   }
 }
 
@@ -768,10 +945,45 @@ __global__ __launch_bounds__(256) void pooled_to_bf16_kernel(const float* __rest
   }
 }
 
-size_t attn_workspace_bytes(const Plan& p) {
-  // pooled keys as hi/lo bf16 pairs, pooled values as bf16
+static int rows_per_unit(const Plan& p) {
+  const int rows = p.g * p.B;
+  return rows >= 256 ? 256 : rows >= 128 ? 128 : 64;  // the launch table below
+}
+
+int attn_splits(const Plan& p, int dtype, int requested) {
+  // work items carry the segment in 23 bits
+  if (dtype == kF32 || requested == 1 || p.num_segments >= (1 << 23)) return 1;
+  if (requested >= 2) return requested;
+  // automatic: when the launch holds fewer than about two workgroups per CU
+  // and some tile can select enough blocks to be worth cutting, split until
+  // it does (at most 4 ways)
+  int64_t units = 0;
+  const int ups = (p.g * p.B + rows_per_unit(p) - 1) / rows_per_unit(p);
+  for (int i = 0; i < p.num_seqs; ++i) units += (int64_t)p.seq[i].nblk * p.hkv * ups;
+  constexpr int64_t kTarget = 512;  // 2 x 256 CUs
+  if (units == 0 || units >= kTarget || p.max_nblk < 16) return 1;
+  return (int)std::min<int64_t>(4, (kTarget + units - 1) / units);
+}
+
+// pooled keys as hi/lo bf16 pairs and pooled values as bf16, then (split
+// launches) the per-split partial O (float32 [splits, T * Hq, d]) and (m, l)
+// pairs (float32 [splits, T * Hq, 2])
+size_t attn_pooled_bytes(const Plan& p) {
   const size_t n = (size_t)p.pooled_rows * p.hkv * p.d;  // elements per pooled tensor
-  return 3 * n * sizeof(uint16_t);
+  return (3 * n * sizeof(uint16_t) + 255) / 256 * 256;
+}
+
+static size_t split_items(const Plan& p, int splits) {
+  const int ups = (p.g * p.B + rows_per_unit(p) - 1) / rows_per_unit(p);
+  return (size_t)p.num_segments * ups * splits;
+}
+
+size_t attn_workspace_bytes(const Plan& p, int splits) {
+  size_t bytes = attn_pooled_bytes(p);
+  if (splits > 1)
+    bytes += (size_t)splits * p.total_tokens * p.hq * (p.d + 2) * sizeof(float) +
+             (split_items(p, splits) + 4) * sizeof(int32_t);
+  return bytes;
 }
 
 template <int DT, int D, int NW, int RT>
@@ -802,10 +1014,40 @@ static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs&
   }
   // logits of the codes: softmax_scale * q_scale * k_scale, in units of log2
   const float c = (float)((double)a.lscale * (double)a.k_scale * 1.4426950408889634);
-  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT>), dim3((unsigned)base), dim3(NW * 64), 0,
-                     st, pl, kv, a.q, a.k, a.v, (const uint16_t*)kb2, (const uint16_t*)vb16, a.cu,
-                     a.idx, c, a.v_scale, a.correction && !a.dense, a.dense, units_per_seg,
-                     (uint16_t*)a.out, a.lse);
+  const int splits = a.splits;
+  const int corr = a.correction && !a.dense;
+  if (splits == 1) {
+    hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT>), dim3((unsigned)base), dim3(NW * 64), 0,
+                       st, pl, kv, a.q, a.k, a.v, (const uint16_t*)kb2, (const uint16_t*)vb16,
+                       a.cu, a.idx, c, a.v_scale, corr, a.dense, units_per_seg, 1,
+                       (uint16_t*)a.out, a.lse, nullptr, nullptr, nullptr, nullptr);
+    return hipGetLastError();
+  }
+  float* part_o = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + attn_pooled_bytes(p));
+  float* part_ml = part_o + (size_t)splits * p.total_tokens * p.hq * D;
+  int32_t* items = reinterpret_cast<int32_t*>(part_ml + (size_t)splits * p.total_tokens * p.hq * 2);
+  int* queue = items + split_items(p, splits);
+  hipLaunchKernelGGL(split_items_kernel, dim3(1), dim3(1024), 0, st, pl, a.cu, splits, corr,
+                     units_per_seg, items, queue);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // persistent workgroups: as many as stay resident at once
+  int dev = 0, cus = 0, per_cu = 0;
+  e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(&attn_mfma_kernel<DT, D, NW, RT>), NW * 64, 0);
+  if (e != hipSuccess) return e;
+  const int64_t grid = std::min<int64_t>(split_items(p, splits), (int64_t)cus * std::max(1, per_cu));
+  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                     st, pl, kv, a.q, a.k, a.v, (const uint16_t*)kb2, (const uint16_t*)vb16,
+                     a.cu, a.idx, c, a.v_scale, corr, a.dense, units_per_seg, splits,
+                     (uint16_t*)a.out, a.lse, part_o, part_ml, items, queue);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_splits_kernel<D>), dim3((unsigned)p.num_segments), dim3(256), 0, st,
+                     p, a.cu, part_o, part_ml, splits, corr, (uint16_t*)a.out, a.lse);
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@ namespace bslp {
 constexpr int kMaxSeqs = 64;
 constexpr int kMaxBlocksPerSeq = 16384;
 constexpr int kMaxGroup = 16;
+constexpr int kMaxSplits = 16;  // KV splits per attention work unit
 
 enum DType : int32_t { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 

@@ -21,7 +21,8 @@ struct AttnArgs {
   float k_scale;  // 1 unless fp8
   float v_scale;
   int correction;
-  int dense;  // walk every causal block J <= I (cu, idx, kbar, vbar unused)
+  int dense;   // walk every causal block J <= I (cu, idx, kbar, vbar unused)
+  int splits;  // KV splits per work unit (1: none), from attn_splits
 };
 
 hipError_t launch_stage1(const Plan& p, const KVDesc& kv, int dtype, const void* q, const void* k,
@@ -41,8 +42,14 @@ hipError_t launch_select(const Plan& p, const SelectArgs& a, const float* scores
 hipError_t launch_attn_valu(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
                             hipStream_t st);
 
-// Device scratch the attention launch needs (bf16 copies of the pooled means).
-size_t attn_workspace_bytes(const Plan& p);
+// KV splits per attention work unit for a requested count (0: automatic, 1:
+// none, 2..kMaxSplits: that many); 1 for the float32 path.
+int attn_splits(const Plan& p, int dtype, int requested);
+
+// Device scratch the attention launch needs: bf16 copies of the pooled means
+// and, for split launches, the per-split partial results.
+size_t attn_pooled_bytes(const Plan& p);
+size_t attn_workspace_bytes(const Plan& p, int splits);
 
 // bf16 and fp8 inputs on the matrix cores (fp8 codes widen exactly to bf16).
 hipError_t launch_attn_mfma(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,

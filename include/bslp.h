@@ -88,6 +88,14 @@ typedef struct bslp_problem {
   const int32_t* page_table; /* DEVICE [num_seqs, max_pages_per_seq] or NULL */
   int32_t page_size;
   int32_t max_pages_per_seq;
+  /* KV splitting of the attention ("FlashPrefill V2", Sec. 3.3: a work unit's
+   * selected blocks are cut into contiguous shares balanced by count, each
+   * run by its own workgroup, and the partial results are merged through
+   * their log-sum-exp).  0 = automatic (split only when the launch has fewer
+   * than about two workgroups per CU), 1 = never, 2..16 = that many splits.
+   * bf16 / fp8 only; the float32 path never splits.  It changes
+   * bslp_sizes.workspace_bytes. */
+  int32_t kv_splits;
 } bslp_problem;
 
 /* Selection hyper-parameters (FlashPrefill V2, Sec. 3.1 and Sec. 4: alpha and

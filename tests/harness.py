@@ -58,14 +58,16 @@ def to_device(inp):
     return inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), table
 
 
-def run_gpu(w: Workload, inp, alpha=None, correction=None, dev_tensors=None) -> GpuResult:
+def run_gpu(w: Workload, inp, alpha=None, correction=None, dev_tensors=None,
+            kv_splits: int = 0) -> GpuResult:
     import torch
 
     import block_sparse_long_pooled_amd as bslp
     q, k, v, table = dev_tensors or to_device(inp)
     prob = bslp.make_problem(w.dtype, w.hq, w.hkv, w.d, w.block, w.seqlens,
                              softmax_scale=w.scale, q_scale=inp.q_scale, k_scale=inp.k_scale,
-                             v_scale=inp.v_scale, page_table=table, page_size=w.page_size)
+                             v_scale=inp.v_scale, page_table=table, page_size=w.page_size,
+                             kv_splits=kv_splits)
     params = bslp.make_params(w.alpha if alpha is None else alpha, w.sink, w.window, w.recent,
                               w.correction if correction is None else correction)
     bufs = bslp.Buffers(prob)

@@ -176,3 +176,35 @@ def test_dense_attention_validated_before_launch():
     assert st == 2
     # nothing to do for an empty problem, so NULL pointers are fine
     bslp.dense_prefill_attn(_problem(seqlens=[0]), None, None, None, None, stream=0)
+
+
+def test_kv_splits_validated_and_sized():
+    st, d = _status(lambda: bslp.get_sizes(_problem(kv_splits=17)))
+    assert st == 1 and "kv_splits" in d
+    st, _ = _status(lambda: bslp.get_sizes(_problem(kv_splits=-1)))
+    assert st == 1
+    base = bslp.get_sizes(_problem(kv_splits=1))
+    assert base.workspace_bytes == bslp.get_sizes(_problem()).workspace_bytes  # small: no split
+    for u in (2, 5):
+        s = bslp.get_sizes(_problem(kv_splits=u))
+        # per split: float32 O [T*Hq, d] and (m, l) [T*Hq, 2] after the pooled
+        # copies, then the work list (an int32 per segment x row block x split)
+        # and its two counters (+2 spare)
+        items = s.num_segments * 2 * u + 4  # g*B = 512 rows: 2 row blocks of 256
+        assert s.workspace_bytes == (base.workspace_bytes + u * s.total_tokens * 8 * (128 + 2) * 4
+                                     + items * 4)
+    # float32 never splits
+    f = bslp.get_sizes(_problem(dtype="f32", kv_splits=4))
+    assert f.workspace_bytes == bslp.get_sizes(_problem(dtype="f32", kv_splits=1)).workspace_bytes
+
+
+def test_automatic_kv_splits_only_for_small_launches():
+    # 16K tokens, one KV head of four query heads: 128 tiles x 2 row blocks
+    small = bslp.get_sizes(_problem(hq=4, hkv=1, seqlens=[16384]))
+    none = bslp.get_sizes(_problem(hq=4, hkv=1, seqlens=[16384], kv_splits=1))
+    assert small.workspace_bytes == (none.workspace_bytes + 2 * 16384 * 4 * 130 * 4
+                                     + (small.num_segments * 2 * 2 + 4) * 4)
+    # 64K tokens x 8 KV heads: thousands of units, no split
+    big = bslp.get_sizes(_problem(hq=32, hkv=8, seqlens=[65536]))
+    assert big.workspace_bytes == bslp.get_sizes(
+        _problem(hq=32, hkv=8, seqlens=[65536], kv_splits=1)).workspace_bytes

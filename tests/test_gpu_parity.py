@@ -100,22 +100,23 @@ def test_paged_equals_contiguous_bitwise():
         assert np.array_equal(a, b, equal_nan=True), name
 
 
-def test_varlen_equals_standalone_bitwise():
+@pytest.mark.parametrize("kv_splits", [1, 3])
+def test_varlen_equals_standalone_bitwise(kv_splits):
+    # with a fixed split count every request's work is cut the same way
+    # whatever it is packed with (the automatic count depends on the batch)
     lens = (640, 1000, 256)
     w = Workload("vl", lens, 8, 2, 128, 64, "bf16", attractors=4)
     inp = make_inputs(w, 2)
-    g = run_gpu(w, inp)
-    import torch
+    g = run_gpu(w, inp, kv_splits=kv_splits)
     starts = np.concatenate([[0], np.cumsum(lens)])
     for b, L in enumerate(lens):
         wb = w.replace(seqlens=(L,))
         sl = slice(int(starts[b]), int(starts[b + 1]))
         inp_b = make_inputs(w, 2)  # same draws; take request b's rows
         inp_b.q, inp_b.k, inp_b.v = (t[sl].contiguous() for t in (inp.q, inp.k, inp.v))
-        gb = run_gpu(wb, inp_b)
+        gb = run_gpu(wb, inp_b, kv_splits=kv_splits)
         assert np.array_equal(gb.out, g.out[sl], equal_nan=True)
         assert np.array_equal(gb.lse, g.lse[:, sl], equal_nan=True)
-    del torch
 
 
 def test_deterministic_bitwise():

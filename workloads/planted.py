@@ -94,6 +94,10 @@ FP8_128K = Workload("gqa-fp8-L131072-hq32-hkv4", (131072,), 32, 4, 128, 128, "fp
 PAGED_VARLEN = Workload("paged-varlen-6req-bf16-hq32-hkv8",
                         (4096, 8192, 32768, 65536, 131072, 262144), 32, 8, 128, 128,
                         "bf16", attractors=4, vertical=8, page_size=128)
+# One GPU's share of the 16K GQA layer under 8-way head sharding: few work
+# units, the case KV splitting is for.
+SHARD_BF16_16K = Workload("tp8-shard-bf16-L16384-hq4-hkv1", (16384,), 4, 1, 128, 128, "bf16",
+                          attractors=4, vertical=8)
 SWEEP_ALPHAS = (0.2, 0.1, 0.05, 0.025, 0.0125)
 
 
