@@ -9,7 +9,8 @@ code with the HIP library and imports nothing from it.
 Every function follows the steps the pages state, in their order and notation,
 with numpy float64 arithmetic; matrix products (`@`) are the only library
 primitive used.  See `flashprefill.py` for the step-by-step citations and
-`fp8.py` for the e4m3 decoder used to read fp8 inputs.
+`fp8.py` for the e4m3 decoder used to read fp8 inputs and the encoder of the
+online per-tensor quantisation.
 
 Pinned by the `-m "not gpu"` tests in `tests/test_oracle_pins.py`.  One part is
 "parity unpinned": the absolute accuracy of the fp8 path against the pages'
@@ -20,9 +21,9 @@ from .flashprefill import (attend_rows, block_scores_row, dense_causal_reference
                            forced_blocks, merge_partials, n_blocks, packgqa_rows,
                            pool_means, request_oracle, select_row, tile_query_rows,
                            todo_row, wasted_row_fraction)
-from .fp8 import decode_e4m3fn
+from .fp8 import decode_e4m3fn, encode_e4m3fn, quantize_per_tensor
 
 __all__ = ["attend_rows", "block_scores_row", "dense_causal_reference", "forced_blocks",
            "merge_partials", "n_blocks", "packgqa_rows", "pool_means", "request_oracle",
            "select_row", "tile_query_rows", "todo_row", "wasted_row_fraction",
-           "decode_e4m3fn"]
+           "decode_e4m3fn", "encode_e4m3fn", "quantize_per_tensor"]

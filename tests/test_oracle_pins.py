@@ -417,3 +417,45 @@ def test_fp8_decoder_matches_torch():
     assert np.array_equal(nan, np.isnan(ours))
     np.testing.assert_array_equal(ours[~nan], ref[~nan])
     assert np.nanmax(ours) == 448.0 and ours[1] == 2.0 ** -9
+
+
+# ---------------------------------------------------------------- online fp8 quantisation
+
+def test_e4m3_encoder_round_trips_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.decode_e4m3fn(codes)
+    ok = ~np.isnan(vals)
+    assert np.array_equal(oracle.encode_e4m3fn(vals[ok]), codes[ok])
+
+
+def test_e4m3_encoder_rounds_to_nearest_even_and_saturates():
+    # 1.0 = 0x38, 1.125 = 0x39, 1.25 = 0x3A: midpoints go to the even code
+    assert oracle.encode_e4m3fn([1.0625, 1.1875])[0] == 0x38
+    assert oracle.encode_e4m3fn([1.1875])[0] == 0x3A
+    assert oracle.encode_e4m3fn([1.0624, 1.0626]).tolist() == [0x38, 0x39]
+    # the smallest subnormal is 2^-9 (0x01); half of it ties to zero, a bit more rounds up
+    assert oracle.encode_e4m3fn([2.0 ** -10, 2.0 ** -10 * 1.01]).tolist() == [0x00, 0x01]
+    # above 448 (0x7E) saturates, with the sign kept
+    assert oracle.encode_e4m3fn([464.0, 1e30, -1e30]).tolist() == [0x7E, 0x7E, 0xFE]
+
+
+def test_e4m3_encoder_matches_torch_cast():
+    import torch
+    x = np.random.default_rng(3).standard_normal(20000).astype(np.float32) * 60
+    ref = torch.from_numpy(x).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.encode_e4m3fn(x), ref)
+
+
+def test_quantize_per_tensor_scale_and_error():
+    x = np.random.default_rng(4).standard_normal(5000).astype(np.float32) * 3
+    codes, scale = oracle.quantize_per_tensor(x)
+    assert scale == np.float32(np.float32(np.abs(x).max()) / np.float32(448))
+    # the absmax element lands on 448 exactly
+    i = int(np.argmax(np.abs(x)))
+    assert abs(oracle.decode_e4m3fn(codes[i])) == 448.0
+    # every other element within half an e4m3 step (relative 2^-4, or the subnormal step)
+    back = oracle.decode_e4m3fn(codes) * float(scale)
+    step = np.maximum(np.abs(x) * 2.0 ** -3, 2.0 ** -9 * float(scale))
+    assert np.all(np.abs(back - x) <= 0.5 * step + 1e-12)
+    z_codes, z_scale = oracle.quantize_per_tensor(np.zeros(7, np.float32))
+    assert z_scale == 1.0 and not z_codes.any()
