@@ -50,6 +50,7 @@ class Problem(ctypes.Structure):
         ("page_size", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32),
         ("kv_splits", ctypes.c_int32),
+        ("scales_dev", ctypes.c_void_p),
     ]
 
 
@@ -74,8 +75,8 @@ class Sizes(ctypes.Structure):
 
 
 EXPORTS = ("bslp_get_sizes", "bslp_block_scores", "bslp_select_blocks",
-           "bslp_sparse_prefill_attn", "bslp_dense_prefill_attn", "bslp_status_string",
-           "bslp_last_error")
+           "bslp_sparse_prefill_attn", "bslp_dense_prefill_attn", "bslp_quantize_e4m3",
+           "bslp_status_string", "bslp_last_error")
 
 _lib = None
 
@@ -97,8 +98,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bslp_sparse_prefill_attn.argtypes = [P(Problem), P(SelectParams), vp, vp, vp, vp, vp,
                                              vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.bslp_dense_prefill_attn.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp]
+    lib.bslp_quantize_e4m3.argtypes = [ctypes.c_int32, vp, ctypes.c_int64, vp, vp, vp]
     for name in ("bslp_get_sizes", "bslp_block_scores", "bslp_select_blocks",
-                 "bslp_sparse_prefill_attn", "bslp_dense_prefill_attn"):
+                 "bslp_sparse_prefill_attn", "bslp_dense_prefill_attn", "bslp_quantize_e4m3"):
         getattr(lib, name).restype = ctypes.c_int
     lib.bslp_status_string.argtypes = [ctypes.c_int]
     lib.bslp_status_string.restype = ctypes.c_char_p
@@ -116,10 +118,12 @@ def _check(status: int):
 def make_problem(dtype: str, hq: int, hkv: int, head_dim: int, block_size: int, seqlens,
                  softmax_scale: float | None = None, q_scale: float = 1.0, k_scale: float = 1.0,
                  v_scale: float = 1.0, page_table=None, page_size: int = 0,
-                 kv_splits: int = 0) -> Problem:
+                 kv_splits: int = 0, scales_dev=None) -> Problem:
     """Fills the problem descriptor.  `page_table` is a device int32 tensor
     [num_seqs, max_pages] (or None for contiguous K/V); `kv_splits` 0 lets the
-    library choose the attention's KV splits, 1 turns them off."""
+    library choose the attention's KV splits, 1 turns them off; `scales_dev`
+    (fp8) is a device float32 tensor of (q, k, v) scales that replaces the
+    host scales, e.g. filled by quantize_e4m3."""
     lens = (ctypes.c_int32 * len(seqlens))(*[int(x) for x in seqlens])
     p = Problem()
     p.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
@@ -129,8 +133,10 @@ def make_problem(dtype: str, hq: int, hkv: int, head_dim: int, block_size: int, 
     p.q_scale, p.k_scale, p.v_scale = q_scale, k_scale, v_scale
     p.num_seqs = len(seqlens)
     p.kv_splits = kv_splits
+    if scales_dev is not None:
+        p.scales_dev = scales_dev.data_ptr()
     p.seqlens = lens
-    p._keep = [lens, page_table]
+    p._keep = [lens, page_table, scales_dev]
     if page_table is not None:
         p.page_table = page_table.data_ptr()
         p.page_size = page_size
@@ -188,6 +194,15 @@ def sparse_prefill_attn(problem, params, q, k, v, kbar, vbar, cu, idx, out, lse=
                                                    _stream(stream)))
 
 
+def quantize_e4m3(x, codes, scale, stream=None):
+    """Online per-tensor e4m3 quantisation of the bf16 or float32 device
+    tensor x into the uint8 tensor codes; scale (a one-element device float32
+    tensor, or a view of one) receives amax / 448."""
+    dt = {"torch.bfloat16": BF16, "torch.float32": F32}[str(x.dtype)]
+    _check(load_library().bslp_quantize_e4m3(dt, _ptr(x), x.numel(), _ptr(codes), _ptr(scale),
+                                             _stream(stream)))
+
+
 def dense_prefill_attn(problem, q, k, v, out, lse=None, stream=None):
     """Dense causal attention over every key j <= i (no index stage)."""
     _check(load_library().bslp_dense_prefill_attn(ctypes.byref(problem), _ptr(q), _ptr(k),
@@ -230,4 +245,4 @@ def prefill(problem, params, q, k, v, bufs: Buffers | None = None, stream=None) 
 __all__ = ["BF16", "F32", "FP8_E4M3", "BslpError", "Buffers", "EXPORTS", "LIB_PATH", "Problem",
            "SelectParams", "Sizes", "block_scores", "dense_prefill_attn", "get_sizes",
            "load_library", "make_params",
-           "make_problem", "prefill", "select_blocks", "sparse_prefill_attn"]
+           "make_problem", "prefill", "quantize_e4m3", "select_blocks", "sparse_prefill_attn"]

@@ -18,6 +18,13 @@ bslp_status fail(bslp_status s, const std::string& msg) {
 
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
 
+// The q / k / v scale the host formulas use: 1 when the scales live in
+// device memory (the kernels apply those themselves).
+float host_scale(const bslp_problem* pr, int which) {
+  if (pr->scales_dev) return 1.f;
+  return which == 0 ? pr->q_scale : which == 1 ? pr->k_scale : pr->v_scale;
+}
+
 bslp_status build_plan(const bslp_problem* pr, bslp::Plan* plan, bslp::KVDesc* kv) {
   if (!pr) return fail(BSLP_ERR_INVALID_ARG, "problem is NULL");
   if (pr->dtype < BSLP_F32 || pr->dtype > BSLP_FP8_E4M3)
@@ -55,11 +62,16 @@ bslp_status build_plan(const bslp_problem* pr, bslp::Plan* plan, bslp::KVDesc* k
   }
   if (pr->kv_splits < 0 || pr->kv_splits > bslp::kMaxSplits)
     return fail(BSLP_ERR_INVALID_ARG, "kv_splits must be in 0 .. 16");
+  if (pr->scales_dev && pr->dtype != BSLP_FP8_E4M3)
+    return fail(BSLP_ERR_INVALID_ARG, "scales_dev is for fp8 inputs only");
+  if (reinterpret_cast<uintptr_t>(pr->scales_dev) % 4)
+    return fail(BSLP_ERR_INVALID_ARG, "scales_dev must be 4-byte aligned");
 
   *plan = bslp::Plan{};
   plan->num_seqs = pr->num_seqs;
   plan->hq = pr->num_heads_q;
   plan->hkv = pr->num_heads_kv;
+  plan->dscale = pr->scales_dev;
   plan->g = g;
   plan->d = pr->head_dim;
   plan->B = pr->block_size;
@@ -159,8 +171,8 @@ bslp_status bslp_block_scores(const bslp_problem* problem, const void* q, const 
   if (plan.total_tokens == 0) return BSLP_OK;
   if (!q || !k || !v || !kbar || !vbar || !scores)
     return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
-  return hip_result(bslp::launch_stage1(plan, kv, problem->dtype, q, k, v, problem->q_scale,
-                                        problem->k_scale, problem->v_scale,
+  return hip_result(bslp::launch_stage1(plan, kv, problem->dtype, q, k, v, host_scale(problem, 0),
+                                        host_scale(problem, 1), host_scale(problem, 2),
                                         problem->softmax_scale, kbar, vbar, scores,
                                         (hipStream_t)stream),
                     "bslp_block_scores");
@@ -209,8 +221,8 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
   if (reinterpret_cast<uintptr_t>(workspace) % 16)
     return fail(BSLP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   bslp::AttnArgs a{q, k, v, kbar, vbar, cu, idx, out, lse, workspace,
-                   problem->softmax_scale * problem->q_scale, problem->k_scale,
-                   problem->v_scale, sa.correction, 0, splits};
+                   problem->softmax_scale * host_scale(problem, 0), host_scale(problem, 1),
+                   host_scale(problem, 2), sa.correction, 0, splits};
   // bf16 and fp8 run on the matrix cores; float32 keeps exact fp32
   // arithmetic on the vector ALUs.
   const hipError_t e = problem->dtype == BSLP_F32
@@ -230,14 +242,28 @@ bslp_status bslp_dense_prefill_attn(const bslp_problem* problem, const void* q, 
   if (plan.total_tokens == 0) return BSLP_OK;
   if (!q || !k || !v || !out) return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
   bslp::AttnArgs a{q, k, v, nullptr, nullptr, nullptr, nullptr, out, lse, nullptr,
-                   problem->softmax_scale * problem->q_scale, problem->k_scale,
-                   problem->v_scale, 0, 1, 1};
+                   problem->softmax_scale * host_scale(problem, 0), host_scale(problem, 1),
+                   host_scale(problem, 2), 0, 1, 1};
   const hipError_t e = problem->dtype == BSLP_F32
                            ? bslp::launch_attn_valu(plan, kv, problem->dtype, a,
                                                     (hipStream_t)stream)
                            : bslp::launch_attn_mfma(plan, kv, problem->dtype, a,
                                                     (hipStream_t)stream);
   return hip_result(e, "bslp_dense_prefill_attn");
+}
+
+bslp_status bslp_quantize_e4m3(int32_t src_dtype, const void* x, int64_t n, uint8_t* codes,
+                               float* scale, void* stream) {
+  if (src_dtype != BSLP_BF16 && src_dtype != BSLP_F32)
+    return fail(BSLP_ERR_INVALID_ARG, "src_dtype must be BSLP_BF16 or BSLP_F32");
+  if (n < 0) return fail(BSLP_ERR_INVALID_ARG, "n must be >= 0");
+  if (!scale || (n > 0 && (!x || !codes)))
+    return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(codes) % 8 ||
+      reinterpret_cast<uintptr_t>(scale) % 4)
+    return fail(BSLP_ERR_INVALID_ARG, "x must be 16-byte, codes 8-byte, scale 4-byte aligned");
+  return hip_result(bslp::launch_quantize_e4m3(src_dtype, x, n, codes, scale, (hipStream_t)stream),
+                    "bslp_quantize_e4m3");
 }
 
 const char* bslp_status_string(bslp_status status) {

@@ -585,6 +585,10 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ items,
     int* __restrict__ queue) {
   using C = AttnCfg<D, NW, RT>;
+  if (p.dscale) {  // fp8 scales kept on the device
+    c *= p.dscale[0] * p.dscale[1];
+    out_scale = p.dscale[2];
+  }
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKeys * C::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VLD];
   __shared__ uint32_t selbits[kMaxBlocksPerSeq / 32];
@@ -916,8 +920,13 @@ __global__ __launch_bounds__(256) void pooled_to_bf16_kernel(const float* __rest
                                                             const float* __restrict__ vbar,
                                                             int64_t n8, int row8, float k_inv,
                                                             float v_inv,
+                                                            const float* __restrict__ dscale,
                                                             uint16_t* __restrict__ kb2,
                                                             uint16_t* __restrict__ vb16) {
+  if (dscale) {
+    k_inv = 1.f / dscale[1];
+    v_inv = 1.f / dscale[2];
+  }
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= 2 * n8) return;
   const bool is_v = i >= n8;
@@ -1008,7 +1017,7 @@ static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs&
     const int64_t n8 = (int64_t)(n / 8);
     hipLaunchKernelGGL(pooled_to_bf16_kernel, dim3((unsigned)((2 * n8 + 255) / 256)), dim3(256),
                        0, st, a.kbar, a.vbar, n8, p.hkv * p.d / 8, 1.f / a.k_scale,
-                       1.f / a.v_scale, kb2, vb16);
+                       1.f / a.v_scale, p.dscale, kb2, vb16);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -33,6 +33,8 @@ struct Plan {
   int64_t total_tokens, pooled_rows, score_elems, num_segments;
   SeqInfo seq[kMaxSeqs];
   int32_t order[kMaxSeqs];  // requests by descending block count (ties: packed order)
+  // fp8 scales (q, k, v) in device memory, or nullptr: the host floats apply
+  const float* dscale;
 };
 
 // Where key/value token j of request b lives.

@@ -51,6 +51,10 @@ int attn_splits(const Plan& p, int dtype, int requested);
 size_t attn_pooled_bytes(const Plan& p);
 size_t attn_workspace_bytes(const Plan& p, int splits);
 
+// Online per-tensor e4m3 quantisation: scale (device, one float) and codes.
+hipError_t launch_quantize_e4m3(int src_dtype, const void* x, int64_t n, uint8_t* codes,
+                                float* scale, hipStream_t st);
+
 // bf16 and fp8 inputs on the matrix cores (fp8 codes widen exactly to bf16).
 hipError_t launch_attn_mfma(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
                             hipStream_t st);

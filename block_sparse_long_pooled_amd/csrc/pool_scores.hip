@@ -43,7 +43,8 @@ __global__ __launch_bounds__(256) void pool_kernel(Plan p, KVDesc kv,
     float t = part[0][col];
 #pragma unroll
     for (int g2 = 1; g2 < RG; ++g2) t += part[g2][col];
-    const float mean = t / (float)cnt * (is_v ? v_scale : k_scale);
+    const float sc = p.dscale ? p.dscale[is_v ? 2 : 1] : (is_v ? v_scale : k_scale);
+    const float mean = t / (float)cnt * sc;
     float* out = is_v ? vbar : kbar;
     out[((int64_t)prow * p.hkv + h) * D + col] = mean;
   }
@@ -68,6 +69,7 @@ __global__ __launch_bounds__(256) void scores_kernel(Plan p,
                                                      const typename Elem<DT>::T* __restrict__ q,
                                                      const float* __restrict__ kbar, double lscale,
                                                      float* __restrict__ scores) {
+  if (p.dscale) lscale *= (double)p.dscale[0];
   constexpr int CH = 32;
   constexpr int NT = 256;
   constexpr int RG = NT / CH;  // row groups

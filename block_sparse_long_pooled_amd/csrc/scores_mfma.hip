@@ -91,6 +91,7 @@ __global__ __launch_bounds__(NW * 64) void scores_mfma_kernel(Plan p,
                                                               const typename Elem<DT>::T* __restrict__ q,
                                                               const float* __restrict__ kbar,
                                                               float c2, float* __restrict__ scores) {
+  if (p.dscale) c2 *= p.dscale[0];  // fp8 q scale kept on the device
   constexpr int NT = NW * 64;
   constexpr int KS = D / 16;            // k-steps of 16 dims
   constexpr int LD = D + 8;             // padded LDS row (bf16), 16-byte multiple

@@ -96,6 +96,11 @@ typedef struct bslp_problem {
    * bf16 / fp8 only; the float32 path never splits.  It changes
    * bslp_sizes.workspace_bytes. */
   int32_t kv_splits;
+  /* fp8 only: DEVICE float[3] = (q_scale, k_scale, v_scale), as written by
+   * bslp_quantize_e4m3, or NULL to use the host floats above (then ignored).
+   * Read by the kernels, so no host synchronisation is needed between the
+   * quantisation and the prefill. */
+  const float* scales_dev;
 } bslp_problem;
 
 /* Selection hyper-parameters (FlashPrefill V2, Sec. 3.1 and Sec. 4: alpha and
@@ -193,6 +198,22 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
  * in the same order.  Errors: as bslp_sparse_prefill_attn. */
 bslp_status bslp_dense_prefill_attn(const bslp_problem* problem, const void* q, const void* k,
                                     const void* v, void* out, float* lse, void* stream);
+
+/* Online per-tensor fp8 quantisation ("FlashPrefill V2", Sec. 3.3 FP8
+ * paragraph: e4m3 operands, one absmax-derived scale per tensor, computed on
+ * the device): with amax = max_i |x_i|, *scale = amax / 448 (1 if amax is 0)
+ * and codes[i] = e4m3fn(x_i / *scale), rounded to nearest even, saturated at
+ * +-448, sign kept (float32 division, correctly rounded).
+ *
+ * x: DEVICE, n elements of src_dtype (BSLP_BF16 or BSLP_F32), 16-byte
+ * aligned.  codes: DEVICE uint8 [n], 8-byte aligned.  scale: DEVICE float,
+ * 4-byte aligned; it also serves as the accumulator of the maximum, so
+ * calls that share it must not overlap.  Paged K/V caches are quantised
+ * whole: every one of the n elements counts towards amax.  Four launches on
+ * `stream`; nothing is synchronised.  Errors: invalid dtype, n < 0, NULL or
+ * misaligned pointers (BSLP_ERR_INVALID_ARG, before any launch). */
+bslp_status bslp_quantize_e4m3(int32_t src_dtype, const void* x, int64_t n, uint8_t* codes,
+                               float* scale, void* stream);
 
 /* Static text for a status code. */
 const char* bslp_status_string(bslp_status status);

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(bslp.LIB_PATH),
 def header_functions():
     text = open(os.path.join(ROOT, "include", "bslp.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bslp_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(bslp_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
@@ -208,3 +208,20 @@ def test_automatic_kv_splits_only_for_small_launches():
     big = bslp.get_sizes(_problem(hq=32, hkv=8, seqlens=[65536]))
     assert big.workspace_bytes == bslp.get_sizes(
         _problem(hq=32, hkv=8, seqlens=[65536], kv_splits=1)).workspace_bytes
+
+
+def test_quantize_and_device_scales_validated_before_launch():
+    lib = bslp.load_library()
+    # bad dtype, negative n, NULL and misaligned pointers
+    assert lib.bslp_quantize_e4m3(2, 0x1000, 8, 0x2000, 0x3000, None) == 1
+    assert lib.bslp_quantize_e4m3(1, 0x1000, -1, 0x2000, 0x3000, None) == 1
+    assert lib.bslp_quantize_e4m3(1, None, 8, 0x2000, 0x3000, None) == 1
+    assert lib.bslp_quantize_e4m3(1, 0x1008, 8, 0x2000, 0x3000, None) == 1
+    assert b"aligned" in lib.bslp_last_error()
+    # device scales are for fp8 only, and aligned
+    t = FakeTensor(ptr=0x4000)
+    st, d = _status(lambda: bslp.get_sizes(_problem(dtype="bf16", scales_dev=t)))
+    assert st == 1 and "fp8" in d
+    st, d = _status(lambda: bslp.get_sizes(_problem(dtype="fp8", scales_dev=FakeTensor(ptr=0x4002))))
+    assert st == 1 and "aligned" in d
+    assert bslp.get_sizes(_problem(dtype="fp8", scales_dev=t)).total_tokens == 1300
