@@ -52,15 +52,19 @@ def pool_means(x: np.ndarray, B: int) -> np.ndarray:
     return out
 
 
-def tile_query_rows(q: np.ndarray, h: int, g: int, B: int, I: int):
-    """Rows of selection tile I for KV head h: positions I*B .. min((I+1)*B, L)-1
-    times the g query heads h*g .. h*g+g-1 of the group (PackGQA row order:
-    position-major, head-minor, [V2] PackGQA paragraph).  q: [L, Hq, d].
+def tile_query_rows(q: np.ndarray, h: int, g: int, B: int, I: int, q_off: int = 0):
+    """Rows of selection tile I for KV head h: the query positions inside
+    block I, max(I*B, q_off) .. min((I+1)*B, L)-1, times the g query heads
+    h*g .. h*g+g-1 of the group (PackGQA row order: position-major,
+    head-minor, [V2] PackGQA paragraph).  q: [L - q_off, Hq, d] holds the
+    queries of positions q_off .. L-1, where L is the key count: a whole
+    prompt has q_off = 0, a chunk of a chunked prefill ([V2] integration
+    paragraph) the position of its first query.
     Returns (positions [rows], head index [rows], vectors [rows, d])."""
-    L = q.shape[0]
-    pos = np.arange(I * B, min((I + 1) * B, L))
+    L = q.shape[0] + q_off
+    pos = np.arange(max(I * B, q_off), min((I + 1) * B, L))
     heads = np.arange(h * g, (h + 1) * g)
-    rows = q[pos][:, heads, :].reshape(-1, q.shape[2]).astype(np.float64)
+    rows = q[pos - q_off][:, heads, :].reshape(-1, q.shape[2]).astype(np.float64)
     return np.repeat(pos, g), np.tile(heads, len(pos)), rows
 
 
@@ -191,9 +195,11 @@ def dense_causal_reference(q, k, v, scale: float):
 
 def request_oracle(q, k, v, B: int, scale: float, alpha: float, sink: int, window: int,
                    recent: int, correction: bool, tiles=None, heads=None):
-    """Whole pipeline for one request (L_q = L_kv = L), the steps in the pages' order.
+    """Whole pipeline for one request, the steps in the pages' order.
 
-    q [L, Hq, d], k/v [L, Hkv, d] as float64 (already dequantised).
+    q [Lq, Hq, d], k/v [L, Hkv, d] as float64 (already dequantised); the
+    queries are the last Lq positions (Lq = L for a whole prompt, fewer for a
+    chunk of a chunked prefill, whose index is re-run over its own tiles).
     `tiles` / `heads` restrict the work to some (KV head, tile) pairs; by
     default every pair is computed.
 
@@ -201,10 +207,13 @@ def request_oracle(q, k, v, B: int, scale: float, alpha: float, sink: int, windo
     thresh, sel, todo, and the tile's output rows (positions, query heads,
     O [rows, d], LSE [rows]).
     """
-    L, Hq, d = q.shape
+    Lq, Hq, d = q.shape
+    L = k.shape[0]
+    q_off = L - Lq
     Hkv = k.shape[1]
     g = Hq // Hkv
     N = n_blocks(L, B)
+    I0 = q_off // B if Lq else N  # first tile that holds a query
     kbar = pool_means(k, B)
     vbar = pool_means(v, B)
     out = {"kbar": kbar, "vbar": vbar, "tiles": {}}
@@ -212,8 +221,8 @@ def request_oracle(q, k, v, B: int, scale: float, alpha: float, sink: int, windo
     for h in heads:
         kh = k[:, h, :].astype(np.float64)
         vh = v[:, h, :].astype(np.float64)
-        for I in (range(N) if tiles is None else tiles):
-            pos, hqs, rows = tile_query_rows(q, h, g, B, I)
+        for I in (range(I0, N) if tiles is None else tiles):
+            pos, hqs, rows = tile_query_rows(q, h, g, B, I, q_off)
             score = block_scores_row(rows, kbar[:, h, :], I, scale)
             sel, thresh = select_row(score, I, alpha, sink, window, recent)
             todo = todo_row(sel, I, correction)

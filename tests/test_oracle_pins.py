@@ -459,3 +459,45 @@ def test_quantize_per_tensor_scale_and_error():
     assert np.all(np.abs(back - x) <= 0.5 * step + 1e-12)
     z_codes, z_scale = oracle.quantize_per_tensor(np.zeros(7, np.float32))
     assert z_scale == 1.0 and not z_codes.any()
+
+
+# ---------------------------------------------------------------- chunked prefill
+
+def _planted(L, Hq, Hkv, d, seed):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((L, Hkv, d))
+    v = rng.standard_normal((L, Hkv, d))
+    q = rng.standard_normal((L, Hq, d)) + np.repeat(k, Hq // Hkv, axis=1) * 1.5
+    return q, k, v
+
+
+@pytest.mark.parametrize("alpha,correction", [(0.2, True), (0.05, False), (0.0, True)])
+def test_block_aligned_chunk_reproduces_the_whole_prompt_tiles(alpha, correction):
+    # a chunk that starts on a block boundary has exactly the whole prompt's
+    # tiles I >= i0 (same rows), so scores, selection and outputs agree
+    B, L, off = 16, 150, 64
+    q, k, v = _planted(L, 4, 2, 8, 5)
+    args = (B, 1 / np.sqrt(8), alpha, 1, 1, 1, correction)
+    whole = oracle.request_oracle(q, k, v, *args)
+    chunk = oracle.request_oracle(q[off:], k, v, *args)
+    assert set(chunk["tiles"]) == {(h, I) for h in range(2) for I in range(off // B, 10)}
+    for key, t in chunk["tiles"].items():
+        w = whole["tiles"][key]
+        assert t["sel"] == w["sel"] and t["todo"] == w["todo"]
+        assert np.array_equal(t["pos"], w["pos"]) and np.array_equal(t["score"], w["score"])
+        assert np.array_equal(t["O"], w["O"]) and np.array_equal(t["lse"], w["lse"])
+
+
+def test_unaligned_chunk_dense_rows_are_textbook_attention():
+    # alpha = 0 without correction: every query of a chunk (first tile cut
+    # mid-block) attends to all keys up to its position
+    B, L, off = 16, 100, 37
+    q, k, v = _planted(L, 4, 2, 8, 6)
+    scale = 1 / np.sqrt(8)
+    chunk = oracle.request_oracle(q[off:], k, v, B, scale, 0.0, 1, 1, 1, False)
+    Od, lsed = oracle.dense_causal_reference(q, k, v, scale)
+    first = chunk["tiles"][(0, off // B)]
+    assert first["pos"].min() == off and len(set(first["pos"])) == (off // B + 1) * B - off
+    for t in chunk["tiles"].values():
+        assert np.allclose(t["O"], Od[t["pos"], t["heads"]], atol=1e-12)
+        assert np.allclose(t["lse"], lsed[t["heads"], t["pos"]], atol=1e-12)
