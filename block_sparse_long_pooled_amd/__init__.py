@@ -51,6 +51,7 @@ class Problem(ctypes.Structure):
         ("max_pages_per_seq", ctypes.c_int32),
         ("kv_splits", ctypes.c_int32),
         ("scales_dev", ctypes.c_void_p),
+        ("kv_seqlens", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -71,6 +72,7 @@ class Sizes(ctypes.Structure):
         ("score_elems", ctypes.c_int64),
         ("num_segments", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
+        ("kv_tokens", ctypes.c_int64),
     ]
 
 
@@ -118,12 +120,14 @@ def _check(status: int):
 def make_problem(dtype: str, hq: int, hkv: int, head_dim: int, block_size: int, seqlens,
                  softmax_scale: float | None = None, q_scale: float = 1.0, k_scale: float = 1.0,
                  v_scale: float = 1.0, page_table=None, page_size: int = 0,
-                 kv_splits: int = 0, scales_dev=None) -> Problem:
+                 kv_splits: int = 0, scales_dev=None, kv_seqlens=None) -> Problem:
     """Fills the problem descriptor.  `page_table` is a device int32 tensor
     [num_seqs, max_pages] (or None for contiguous K/V); `kv_splits` 0 lets the
     library choose the attention's KV splits, 1 turns them off; `scales_dev`
     (fp8) is a device float32 tensor of (q, k, v) scales that replaces the
-    host scales, e.g. filled by quantize_e4m3."""
+    host scales, e.g. filled by quantize_e4m3.  `kv_seqlens` gives each
+    request's key count when its queries are only the last `seqlens[b]`
+    positions (a chunk of a chunked prefill)."""
     lens = (ctypes.c_int32 * len(seqlens))(*[int(x) for x in seqlens])
     p = Problem()
     p.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
@@ -136,7 +140,11 @@ def make_problem(dtype: str, hq: int, hkv: int, head_dim: int, block_size: int, 
     if scales_dev is not None:
         p.scales_dev = scales_dev.data_ptr()
     p.seqlens = lens
-    p._keep = [lens, page_table, scales_dev]
+    kvl = None
+    if kv_seqlens is not None:
+        kvl = (ctypes.c_int32 * len(kv_seqlens))(*[int(x) for x in kv_seqlens])
+        p.kv_seqlens = kvl
+    p._keep = [lens, page_table, scales_dev, kvl]
     if page_table is not None:
         p.page_table = page_table.data_ptr()
         p.page_size = page_size

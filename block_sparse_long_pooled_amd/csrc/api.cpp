@@ -75,30 +75,38 @@ bslp_status build_plan(const bslp_problem* pr, bslp::Plan* plan, bslp::KVDesc* k
   plan->g = g;
   plan->d = pr->head_dim;
   plan->B = pr->block_size;
-  int64_t tok = 0, pool = 0, seg = 0, score = 0;
+  int64_t tok = 0, kvtok = 0, pool = 0, seg = 0, score = 0;
   int max_nblk = 0;
   for (int b = 0; b < pr->num_seqs; ++b) {
-    const int64_t L = pr->seqlens[b];
-    if (L < 0) return fail(BSLP_ERR_INVALID_ARG, "negative sequence length");
+    const int64_t Lq = pr->seqlens[b];
+    const int64_t L = pr->kv_seqlens ? pr->kv_seqlens[b] : Lq;
+    if (Lq < 0 || L < 0) return fail(BSLP_ERR_INVALID_ARG, "negative sequence length");
+    if (Lq > L)
+      return fail(BSLP_ERR_INVALID_ARG, "a request has more queries than keys (seqlens > kv_seqlens)");
     const int64_t N = (L + plan->B - 1) / plan->B;
+    const int64_t i0 = Lq > 0 ? (L - Lq) / plan->B : N;  // no query: no tile
     if (N > bslp::kMaxBlocksPerSeq)
       return fail(BSLP_ERR_UNSUPPORTED, "more than 16384 blocks in one request");
     if (pr->page_table && (L + pr->page_size - 1) / pr->page_size > pr->max_pages_per_seq)
       return fail(BSLP_ERR_INVALID_ARG, "request longer than max_pages_per_seq pages");
     bslp::SeqInfo& s = plan->seq[b];
     s.tok_start = (int32_t)tok;
+    s.kv_start = (int32_t)kvtok;
     s.len = (int32_t)L;
+    s.q_off = (int32_t)(L - Lq);
     s.nblk = (int32_t)N;
+    s.i0 = (int32_t)i0;
     s.pool_base = (int32_t)pool;
     s.seg_base = (int32_t)seg;
     s.unit_base = 0;
     s.score_base = score;
-    tok += L;
+    tok += Lq;
+    kvtok += L;
     pool += N;
-    seg += (int64_t)plan->hkv * N;
-    score += (int64_t)plan->hkv * N * (N + 1) / 2;
+    seg += (int64_t)plan->hkv * (N - i0);
+    score += (int64_t)plan->hkv * (N * (N + 1) / 2 - i0 * (i0 + 1) / 2);
     if (N > max_nblk) max_nblk = (int)N;
-    if (tok >= (int64_t(1) << 31) || score >= (int64_t(1) << 31))
+    if (kvtok >= (int64_t(1) << 31) || score >= (int64_t(1) << 31))
       return fail(BSLP_ERR_UNSUPPORTED, "problem exceeds 2^31 tokens or index entries");
   }
   plan->max_nblk = max_nblk;
@@ -112,6 +120,7 @@ bslp_status build_plan(const bslp_problem* pr, bslp::Plan* plan, bslp::KVDesc* k
     plan->order[j] = i;
   }
   plan->total_tokens = tok;
+  plan->kv_tokens = kvtok;
   plan->pooled_rows = pool;
   plan->num_segments = seg;
   plan->score_elems = score;
@@ -153,6 +162,7 @@ bslp_status bslp_get_sizes(const bslp_problem* problem, bslp_sizes* out) {
   const bslp_status st = build_plan(problem, &plan, &kv);
   if (st != BSLP_OK) return st;
   out->total_tokens = plan.total_tokens;
+  out->kv_tokens = plan.kv_tokens;
   out->pooled_rows = plan.pooled_rows;
   out->score_elems = plan.score_elems;
   out->num_segments = plan.num_segments;

@@ -125,7 +125,7 @@ __device__ __forceinline__ void uniform(Step& st) {
 }
 
 struct UnitCtx {
-  int b, h, I, len, tok_start, pool_base, B;
+  int b, h, I, len, kv_start, pool_base, B;  // len: keys of the request
   int beg, end;  // the unit's share of the CSR positions of its segment
   int dense;     // blocks are J = t for t in [0, I]: no index list
   int c0, cstep; // correction chunks c0, c0 + cstep, ... belong to the unit
@@ -340,7 +340,7 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
         const int phys = uni(kv.page_table[(int64_t)u.b * kv.max_pages + (key0 >> kv.page_shift)]);
         row0 = ((int64_t)phys << kv.page_shift) | (int64_t)(key0 & ((1 << kv.page_shift) - 1));
       } else {
-        row0 = (int64_t)u.tok_start + key0;
+        row0 = (int64_t)u.kv_start + key0;
       }
       kb0 = vb0 = (row0 * stride + (int64_t)u.h * D) * esize;
       nrec_k = nrec_v = (last * (int)stride + D) * esize;
@@ -384,11 +384,11 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
   for (int i = 0; i < C::VL; ++i) vkey[i] = min(2 * (min(tid + i * C::NT, C::VPN - 1) % PAIRS), last);
   int64_t krow[C::KL], vrow0[C::VL], vrow1[C::VL];
 #pragma unroll
-  for (int i = 0; i < C::KL; ++i) krow[i] = kv.row(u.b, u.tok_start, key0 + kkey[i]);
+  for (int i = 0; i < C::KL; ++i) krow[i] = kv.row(u.b, u.kv_start, key0 + kkey[i]);
 #pragma unroll
   for (int i = 0; i < C::VL; ++i) {
-    vrow0[i] = kv.row(u.b, u.tok_start, key0 + vkey[i]);
-    vrow1[i] = kv.row(u.b, u.tok_start, key0 + min(vkey[i] + 1, last));
+    vrow0[i] = kv.row(u.b, u.kv_start, key0 + vkey[i]);
+    vrow1[i] = kv.row(u.b, u.kv_start, key0 + min(vkey[i] + 1, last));
   }
   const int64_t hoff = (int64_t)u.h * D;
 #pragma unroll
@@ -602,14 +602,14 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   // One work unit: (segment (b, h, I), row block mt, KV split sp).
   auto run_unit = [&](int b, int I, int h, int mt, int sp) __attribute__((always_inline)) {
   const SeqInfo s = p.seq[b];
-  const int64_t seg = (int64_t)s.seg_base + (int64_t)h * s.nblk + I;
-  const int nb = min(p.B, s.len - I * p.B);
-  const int R = p.g * nb;
+  const int64_t seg = (int64_t)s.seg_base + (int64_t)h * ntile(s) + (I - s.i0);
+  const int q0 = tile_q0(s, I, p.B);
+  const int R = p.g * tile_nq(s, I, p.B);
   // split sp of the segment's ns takes a contiguous share of the CSR
   // positions, balanced by count, and every ns-th correction chunk
   const int beg0 = dense ? 0 : cu[seg], n_sel = (dense ? I + 1 : cu[seg + 1]) - beg0;
   const int ns = splits == 1 ? 1 : segment_splits(n_sel, I, p.B, correction, splits);
-  UnitCtx u{b, h, I, s.len, s.tok_start, s.pool_base, p.B,
+  UnitCtx u{b, h, I, s.len, s.kv_start, s.pool_base, p.B,
             beg0 + (int)((int64_t)sp * n_sel / ns),
             beg0 + (int)((int64_t)(sp + 1) * n_sel / ns), dense, sp, ns};
 
@@ -623,9 +623,9 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   for (int rt = 0; rt < RT; ++rt) {
     const int r = row0 + rt * 32 + (lane & 31);
     valid[rt] = r < R;
-    qpos[rt] = I * p.B + (valid[rt] ? r / p.g : 0);
+    qpos[rt] = q0 + (valid[rt] ? r / p.g : 0);
     hqs[rt] = h * p.g + (valid[rt] ? r % p.g : 0);
-    const int64_t qoff = ((int64_t)(s.tok_start + qpos[rt]) * p.hq + hqs[rt]) * D;
+    const int64_t qoff = (q_row(s, qpos[rt]) * p.hq + hqs[rt]) * D;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       u32x4_t w = {0u, 0u, 0u, 0u};
@@ -731,7 +731,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const float l_tot = halves_sum(l_run[rt]);
     if (!valid[rt]) continue;
     const float inv = l_tot > 0.f ? out_scale / l_tot : 0.f;
-    const int64_t orow = (int64_t)(s.tok_start + qpos[rt]) * p.hq + hqs[rt];
+    const int64_t orow = q_row(s, qpos[rt]) * p.hq + hqs[rt];
     if (ns > 1) {
       const int64_t prow = (int64_t)sp * p.total_tokens * p.hq + orow;
 #pragma unroll
@@ -763,7 +763,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
       }
     }
     if (lse && half == 0)
-      lse[(int64_t)hqs[rt] * p.total_tokens + s.tok_start + qpos[rt]] =
+      lse[(int64_t)hqs[rt] * p.total_tokens + q_row(s, qpos[rt])] =
           l_tot > 0.f ? m_run[rt] * kLn2 + __logf(l_tot) : -INFINITY;
   }
   };
@@ -794,8 +794,9 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const int64_t seg = code >> 8;
     int b = 0;
     while (b + 1 < p.num_seqs && p.seq[b + 1].seg_base <= seg) ++b;
-    const int local = (int)(seg - p.seq[b].seg_base);
-    run_unit(b, local % p.seq[b].nblk, local / p.seq[b].nblk, (code >> 4) & 15, code & 15);
+    int h, I;
+    segment_tile(p.seq[b], (int)(seg - p.seq[b].seg_base), h, I);
+    run_unit(b, I, h, (code >> 4) & 15, code & 15);
   }
 
 }
@@ -815,15 +816,15 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(Plan p, const int32_t
   const int64_t seg = blockIdx.x;
   const int b = seq_of_segment(p, seg);
   const SeqInfo s = p.seq[b];
-  const int local = (int)(seg - s.seg_base);
-  const int h = local / s.nblk, I = local % s.nblk;
+  int h, I;
+  segment_tile(s, (int)(seg - s.seg_base), h, I);
   const int ns = segment_splits(cu[seg + 1] - cu[seg], I, p.B, correction, splits);
   if (ns == 1) return;
-  const int nb = min(p.B, s.len - I * p.B);
+  const int q0 = tile_q0(s, I, p.B), nq = tile_nq(s, I, p.B);
   const int64_t prows = p.total_tokens * p.hq;  // rows of one split's partials
-  for (int i = threadIdx.x; i < p.g * nb * (D / 4); i += 256) {
+  for (int i = threadIdx.x; i < p.g * nq * (D / 4); i += 256) {
     const int r = i / (D / 4), d = (i % (D / 4)) * 4;
-    const int64_t tok = s.tok_start + I * p.B + r / p.g;
+    const int64_t tok = q_row(s, q0 + r / p.g);
     const int hq = h * p.g + r % p.g;
     const int64_t row = tok * p.hq + hq;
     float M = -INFINITY;
@@ -873,14 +874,14 @@ __global__ __launch_bounds__(1024) void split_items_kernel(Plan p, const int32_t
       // q-th segment in launch order
       int i = 0;
       int64_t qb = 0;
-      while (qb + (int64_t)p.seq[p.order[i]].nblk * p.hkv <= q) {
-        qb += (int64_t)p.seq[p.order[i]].nblk * p.hkv;
+      while (qb + (int64_t)ntile(p.seq[p.order[i]]) * p.hkv <= q) {
+        qb += (int64_t)ntile(p.seq[p.order[i]]) * p.hkv;
         ++i;
       }
       const SeqInfo& si = p.seq[p.order[i]];
       const int local = (int)(q - qb);
       I = si.nblk - 1 - local / p.hkv;
-      seg = si.seg_base + (local % p.hkv) * si.nblk + I;
+      seg = si.seg_base + (local % p.hkv) * ntile(si) + (I - si.i0);
       n = segment_splits(cu[seg + 1] - cu[seg], I, p.B, correction, splits) * units_per_seg;
     }
     // block-wide exclusive prefix sum of n
@@ -968,7 +969,7 @@ int attn_splits(const Plan& p, int dtype, int requested) {
   // it does (at most 4 ways)
   int64_t units = 0;
   const int ups = (p.g * p.B + rows_per_unit(p) - 1) / rows_per_unit(p);
-  for (int i = 0; i < p.num_seqs; ++i) units += (int64_t)p.seq[i].nblk * p.hkv * ups;
+  for (int i = 0; i < p.num_seqs; ++i) units += (int64_t)ntile(p.seq[i]) * p.hkv * ups;
   constexpr int64_t kTarget = 512;  // 2 x 256 CUs
   if (units == 0 || units >= kTarget || p.max_nblk < 16) return 1;
   return (int)std::min<int64_t>(4, (kTarget + units - 1) / units);
@@ -1007,7 +1008,7 @@ static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs&
   for (int i = 0; i < pl.num_seqs; ++i) {
     const int b = pl.order[i];
     pl.seq[b].unit_base = (int32_t)base;
-    base += (int64_t)pl.seq[b].nblk * pl.hkv * units_per_seg;
+    base += (int64_t)ntile(pl.seq[b]) * pl.hkv * units_per_seg;
   }
   if (base == 0) return hipSuccess;
   const size_t n = (size_t)p.pooled_rows * p.hkv * p.d;

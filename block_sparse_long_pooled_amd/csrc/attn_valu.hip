@@ -80,20 +80,18 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
   const int mt = (int)(unit % units_per_seg);
   const int b = seq_of_segment(p, seg);
   const SeqInfo s = p.seq[b];
-  const int local = (int)(seg - s.seg_base);
-  const int h = local / s.nblk;
-  const int I = local % s.nblk;
-  const int nb = min(p.B, s.len - I * p.B);
-  const int R = p.g * nb;
+  int h, I;
+  segment_tile(s, (int)(seg - s.seg_base), h, I);
+  const int R = p.g * tile_nq(s, I, p.B);
   if (mt * 64 >= R) return;  // uniform: tile shorter than this unit
   const int r = mt * 64 + lane;
   const bool valid = r < R;
-  const int qpos = valid ? I * p.B + r / p.g : -1;
+  const int qpos = valid ? tile_q0(s, I, p.B) + r / p.g : -1;
   const int hq = h * p.g + (r % p.g);
 
   float qr[D];
   if (valid) {
-    const int64_t qoff = ((int64_t)(s.tok_start + qpos) * p.hq + hq) * D;
+    const int64_t qoff = (q_row(s, qpos) * p.hq + hq) * D;
 #pragma unroll
     for (int c = 0; c < D; c += 8) load8<DT>(q, qoff + c, qr + c);
   } else {
@@ -118,7 +116,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
         const int kk = e / D, c = e % D;
         float kvv = 0.f, vvv = 0.f;
         if (kk < nk) {
-          const int64_t row = kv.row(b, s.tok_start, j0 + sub + kk);
+          const int64_t row = kv.row(b, s.kv_start, j0 + sub + kk);
           const int64_t off = (row * p.hkv + h) * D + c;
           kvv = Elem<DT>::load(k, off) * k_scale;
           vvv = Elem<DT>::load(v, off) * v_scale;
@@ -172,7 +170,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
 
   if (!valid) return;
   const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-  const int64_t ooff = ((int64_t)(s.tok_start + qpos) * p.hq + hq) * D;
+  const int64_t ooff = (q_row(s, qpos) * p.hq + hq) * D;
   if constexpr (DT == kF32) {
     float* o = reinterpret_cast<float*>(out) + ooff;
 #pragma unroll
@@ -182,7 +180,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
 #pragma unroll
     for (int c = 0; c < D; ++c) o[c] = f32_to_bf16(st.o[c] * inv);
   }
-  if (lse) lse[(int64_t)hq * p.total_tokens + s.tok_start + qpos] =
+  if (lse) lse[(int64_t)hq * p.total_tokens + q_row(s, qpos)] =
       st.l > 0.f ? st.m + logf(st.l) : -INFINITY;
 }
 

@@ -16,21 +16,50 @@ constexpr int kMaxSplits = 16;  // KV splits per attention work unit
 enum DType : int32_t { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
 // One packed request.  All bases are prefix sums over earlier requests.
+// Its keys are positions 0 .. len-1; its queries are the last len - q_off of
+// them (a chunk of a chunked prefill; q_off = 0 for a whole prompt), and only
+// the tiles I >= i0 that hold a query are scored, selected and attended.
 struct SeqInfo {
-  int32_t tok_start;   // first token row of the request in Q / O / contiguous K, V
-  int32_t len;         // L_b
-  int32_t nblk;        // N_b = ceil(L_b / B)
+  int32_t tok_start;   // first Q / O row (LSE column) of the request's queries
+  int32_t kv_start;    // first K / V row of the request (contiguous K/V)
+  int32_t len;         // L_b^kv: keys
+  int32_t q_off;       // L_b^kv - L_b^q: position of the first query
+  int32_t nblk;        // N_b = ceil(L_b^kv / B): key blocks
+  int32_t i0;          // first query tile: q_off / B
   int32_t pool_base;   // first pooled row (kbar / vbar)
-  int32_t seg_base;    // first segment: segments are (h, I) with h*N_b + I
+  int32_t seg_base;    // first segment: (h, I) is segment h*(N_b - i0) + I - i0
   int32_t unit_base;   // first work unit of the request (kernel specific use)
   int64_t score_base;  // first score element of the request
 };
+
+__host__ __device__ __forceinline__ int ntile(const SeqInfo& s) { return s.nblk - s.i0; }
+
+// KV head and tile of the request's local segment index.
+__host__ __device__ __forceinline__ void segment_tile(const SeqInfo& s, int local, int& h,
+                                                      int& I) {
+  h = local / ntile(s);
+  I = s.i0 + local % ntile(s);
+}
+
+// Query positions of tile I: tile_q0 .. tile_q0 + tile_nq - 1.
+__host__ __device__ __forceinline__ int tile_q0(const SeqInfo& s, int I, int B) {
+  return I * B > s.q_off ? I * B : s.q_off;
+}
+__host__ __device__ __forceinline__ int tile_nq(const SeqInfo& s, int I, int B) {
+  return ((I + 1) * B < s.len ? (I + 1) * B : s.len) - tile_q0(s, I, B);
+}
+
+// Q / O row (and LSE column) of query position pos.
+__host__ __device__ __forceinline__ int64_t q_row(const SeqInfo& s, int pos) {
+  return (int64_t)s.tok_start + pos - s.q_off;
+}
 
 struct Plan {
   int32_t num_seqs;
   int32_t hq, hkv, g, d, B;
   int32_t max_nblk;
-  int64_t total_tokens, pooled_rows, score_elems, num_segments;
+  int64_t total_tokens, pooled_rows, score_elems, num_segments;  // total_tokens: query rows
+  int64_t kv_tokens;  // key / value rows (contiguous K/V)
   SeqInfo seq[kMaxSeqs];
   int32_t order[kMaxSeqs];  // requests by descending block count (ties: packed order)
   // fp8 scales (q, k, v) in device memory, or nullptr: the host floats apply
@@ -57,8 +86,10 @@ struct SelectArgs {
 
 // Score row of segment (b, h, I) starts here.
 __host__ __device__ __forceinline__ int64_t score_offset(const SeqInfo& s, int h, int I) {
-  return s.score_base + (int64_t)h * ((int64_t)s.nblk * (s.nblk + 1) / 2) +
-         (int64_t)I * (I + 1) / 2;
+  // rows I = i0 .. N-1 of I+1 scores each, per KV head
+  const int64_t first = (int64_t)s.i0 * (s.i0 + 1) / 2;
+  return s.score_base + (int64_t)h * ((int64_t)s.nblk * (s.nblk + 1) / 2 - first) +
+         (int64_t)I * (I + 1) / 2 - first;
 }
 
 // Request owning a segment / unit index (linear scan; at most kMaxSeqs).

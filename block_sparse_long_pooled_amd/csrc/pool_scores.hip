@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void pool_kernel(Plan p, KVDesc kv,
   const typename Elem<DT>::T* x = is_v ? v : k;
   float acc = 0.f;
   for (int r = rg; r < cnt; r += RG) {
-    const int64_t row = kv.row(b, s.tok_start, j0 + r);
+    const int64_t row = kv.row(b, s.kv_start, j0 + r);
     acc += Elem<DT>::load(x, (row * p.hkv + h) * D + col);
   }
   part[rg][col] = acc;
@@ -87,11 +87,10 @@ __global__ __launch_bounds__(256) void scores_kernel(Plan p,
   const int64_t seg = p.num_segments - 1 - (int64_t)blockIdx.x;  // longest rows first
   const int b = seq_of_segment(p, seg);
   const SeqInfo s = p.seq[b];
-  const int local = (int)(seg - s.seg_base);
-  const int h = local / s.nblk;
-  const int I = local % s.nblk;
-  const int nb = min(p.B, s.len - I * p.B);
-  const int R = p.g * nb;
+  int h, I;
+  segment_tile(s, (int)(seg - s.seg_base), h, I);
+  const int q0 = tile_q0(s, I, p.B);
+  const int R = p.g * tile_nq(s, I, p.B);
   const int nJ = I + 1;
   const int nch = (nJ + CH - 1) / CH;
   float* row_out = scores + score_offset(s, h, I);
@@ -110,9 +109,9 @@ __global__ __launch_bounds__(256) void scores_kernel(Plan p,
         kr[cc] = t4.x; kr[cc + 1] = t4.y; kr[cc + 2] = t4.z; kr[cc + 3] = t4.w;
       }
       for (int r = rg; r < R; r += RG) {
-        const int pos = I * p.B + r / p.g;
+        const int pos = q0 + r / p.g;
         const int hq = h * p.g + r % p.g;
-        const int64_t qoff = ((int64_t)(s.tok_start + pos) * p.hq + hq) * D;
+        const int64_t qoff = (q_row(s, pos) * p.hq + hq) * D;
         double acc = 0.0;
 #pragma unroll
         for (int cc = 0; cc < D; cc += 8) {

@@ -111,11 +111,10 @@ __global__ __launch_bounds__(NW * 64) void scores_mfma_kernel(Plan p,
   const int64_t seg = p.num_segments - 1 - (int64_t)blockIdx.x;  // longest rows first
   const int b = seq_of_segment(p, seg);
   const SeqInfo s = p.seq[b];
-  const int local = (int)(seg - s.seg_base);
-  const int h = local / s.nblk;
-  const int I = local % s.nblk;
-  const int nb = min(p.B, s.len - I * p.B);
-  const int R = p.g * nb;
+  int h, I;
+  segment_tile(s, (int)(seg - s.seg_base), h, I);
+  const int q0 = tile_q0(s, I, p.B);
+  const int R = p.g * tile_nq(s, I, p.B);
   const int nJ = I + 1;
   const int nch = (nJ + kChunk - 1) / kChunk;
   float* cmax = dyn;
@@ -132,9 +131,9 @@ __global__ __launch_bounds__(NW * 64) void scores_mfma_kernel(Plan p,
   for (int t = 0; t < RT; ++t) {
     const int r = row0 + t * 32 + jj;
     const bool ok = r < R;
-    const int pos = I * p.B + (ok ? r / p.g : 0);
+    const int pos = q0 + (ok ? r / p.g : 0);
     const int hq = h * p.g + (ok ? r % p.g : 0);
-    const int64_t qoff = ((int64_t)(s.tok_start + pos) * p.hq + hq) * D;
+    const int64_t qoff = (q_row(s, pos) * p.hq + hq) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 u = make_uint4(0, 0, 0, 0);

@@ -24,9 +24,7 @@ __device__ __forceinline__ SegPos segment_position(const Plan& p, int64_t seg) {
   SegPos r;
   r.b = seq_of_segment(p, seg);
   const SeqInfo& s = p.seq[r.b];
-  const int local = (int)(seg - s.seg_base);
-  r.h = local / s.nblk;
-  r.I = local % s.nblk;
+  segment_tile(s, (int)(seg - s.seg_base), r.h, r.I);
   r.off = score_offset(s, r.h, r.I);
   return r;
 }

@@ -29,18 +29,26 @@
  *   failures return BSLP_ERR_HIP.  bslp_last_error() gives a thread-local text
  *   for the last failing call of the calling thread.  No exception crosses
  *   the ABI and there is no global mutable state besides that text.
- * Sequences: requests are packed back to back ("varlen"); request b owns
- *   token rows [start_b, start_b + L_b) with start_b = L_0 + ... + L_{b-1};
- *   queries and keys share positions (self prefill, L_q = L_kv).
- * Blocks: key block J of request b covers tokens [J*B, min((J+1)*B, L_b));
- *   N_b = ceil(L_b / B).  Query tile I covers the same positions for the g =
- *   Hq/Hkv query heads of one KV head (PackGQA rows, FlashPrefill V2 PackGQA
- *   paragraph); one selection is made per (request, KV head, tile).
- * Segments: s(b, h, I) = seg_base_b + h*N_b + I with seg_base_b =
- *   sum_{b'<b} Hkv*N_b'.  Score rows: row (b, h, I) has I+1 floats at
- *   score_base_b + h*N_b(N_b+1)/2 + I(I+1)/2, score_base_b = sum_{b'<b}
- *   Hkv*N_b'(N_b'+1)/2.  Pooled rows: block J of request b is pooled row
- *   pool_base_b + J, pool_base_b = sum_{b'<b} N_b'.
+ * Sequences: requests are packed back to back ("varlen").  Request b has
+ *   L_b = kv_seqlens[b] keys at positions 0 .. L_b - 1 and Lq_b = seqlens[b]
+ *   queries: the last Lq_b positions, off_b = L_b - Lq_b .. L_b - 1 (a chunk
+ *   of a chunked prefill, FlashPrefill V2 integration paragraph; off_b = 0
+ *   for a whole prompt, when kv_seqlens is NULL).  Its queries own Q / O rows
+ *   (and LSE columns) [qstart_b, qstart_b + Lq_b), qstart_b = sum_{b'<b}
+ *   Lq_b'; its keys own contiguous K / V rows [kstart_b, kstart_b + L_b),
+ *   kstart_b = sum_{b'<b} L_b'.
+ * Blocks: key block J of request b covers positions [J*B, min((J+1)*B, L_b));
+ *   N_b = ceil(L_b / B).  Query tile I covers the query positions inside
+ *   block I, for the g = Hq/Hkv query heads of one KV head (PackGQA rows,
+ *   FlashPrefill V2 PackGQA paragraph); the tiles that hold a query are
+ *   I = i0_b .. N_b - 1 with i0_b = floor(off_b / B) (none if Lq_b = 0), and
+ *   one selection is made per (request, KV head, tile), re-run per chunk.
+ * Segments: s(b, h, I) = seg_base_b + h*(N_b - i0_b) + I - i0_b with
+ *   seg_base_b = sum_{b'<b} Hkv*(N_b' - i0_b').  Score rows: row (b, h, I)
+ *   has I+1 floats at score_base_b + h*T_b + I(I+1)/2 - i0_b(i0_b+1)/2, with
+ *   T_b = N_b(N_b+1)/2 - i0_b(i0_b+1)/2 and score_base_b = sum_{b'<b} Hkv*T_b'.
+ *   Pooled rows: block J of request b is pooled row pool_base_b + J,
+ *   pool_base_b = sum_{b'<b} N_b' (every key block is pooled).
  */
 #ifndef BSLP_H
 #define BSLP_H
@@ -78,7 +86,7 @@ typedef struct bslp_problem {
   float k_scale;          /*   fp8 element x decodes to code(x) * scale.     */
   float v_scale;          /*   Must be 1 for f32 / bf16.                     */
   int32_t num_seqs;       /* 1 .. 64                                         */
-  const int32_t* seqlens; /* HOST array [num_seqs], each L_b >= 0, N_b <= 16384 */
+  const int32_t* seqlens; /* HOST array [num_seqs]: queries Lq_b >= 0        */
   /* Paged K/V (FlashPrefill V2, paged-KV paragraph): when page_table is not
    * NULL, key/value token j of request b lives at physical row
    * page_table[b * max_pages_per_seq + j / page_size] * page_size
@@ -101,6 +109,9 @@ typedef struct bslp_problem {
    * Read by the kernels, so no host synchronisation is needed between the
    * quantisation and the prefill. */
   const float* scales_dev;
+  /* HOST array [num_seqs]: keys L_b >= seqlens[b], N_b <= 16384; NULL means
+   * L_b = seqlens[b] (self prefill of whole prompts). */
+  const int32_t* kv_seqlens;
 } bslp_problem;
 
 /* Selection hyper-parameters (FlashPrefill V2, Sec. 3.1 and Sec. 4: alpha and
@@ -119,11 +130,12 @@ typedef struct bslp_select_params {
 
 /* Buffer sizes implied by a problem. */
 typedef struct bslp_sizes {
-  int64_t total_tokens; /* T = sum L_b: rows of Q, O and (contiguous) K/V     */
+  int64_t total_tokens; /* T = sum Lq_b: rows of Q and O, columns of LSE      */
   int64_t pooled_rows;  /* sum N_b: rows of kbar / vbar                       */
-  int64_t score_elems;  /* sum Hkv N_b (N_b+1)/2: scores and idx capacity     */
-  int64_t num_segments; /* sum Hkv N_b: entries of counts (cu has one more)   */
+  int64_t score_elems;  /* sum Hkv T_b: scores and idx capacity               */
+  int64_t num_segments; /* sum Hkv (N_b - i0_b): entries of counts (cu: +1)   */
   int64_t workspace_bytes; /* device scratch bslp_sparse_prefill_attn needs     */
+  int64_t kv_tokens;    /* sum L_b: rows of contiguous K and V                */
 } bslp_sizes;
 
 /* Validates `problem` and fills `out`.  Host only; no HIP call. */

@@ -21,18 +21,23 @@ def log(msg: str):
     sys.stdout.flush()
 
 
-def segments(seqlens, hkv, B):
-    """(b, h, I, segment index, score offset) in the C-ABI layout of bslp.h."""
+def segments(seqlens, hkv, B, q_lens=None):
+    """(b, h, I, segment index, score offset) in the C-ABI layout of bslp.h:
+    per request the tiles I >= i0 that hold a query, I + 1 scores each."""
+    q_lens = seqlens if q_lens is None else q_lens
     out = []
     seg = 0
     sc = 0
-    for b, L in enumerate(seqlens):
+    for b, (L, Lq) in enumerate(zip(seqlens, q_lens)):
         N = -(-L // B)
+        i0 = (L - Lq) // B if Lq else N
+        first = i0 * (i0 + 1) // 2
+        tri = N * (N + 1) // 2 - first
         for h in range(hkv):
-            for I in range(N):
-                out.append((b, h, I, seg + h * N + I, sc + h * N * (N + 1) // 2 + I * (I + 1) // 2))
-        seg += hkv * N
-        sc += hkv * N * (N + 1) // 2
+            for I in range(i0, N):
+                out.append((b, h, I, seg + h * (N - i0) + I - i0, sc + h * tri + I * (I + 1) // 2 - first))
+        seg += hkv * (N - i0)
+        sc += hkv * tri
     return out
 
 
@@ -64,10 +69,11 @@ def run_gpu(w: Workload, inp, alpha=None, correction=None, dev_tensors=None,
 
     import block_sparse_long_pooled_amd as bslp
     q, k, v, table = dev_tensors or to_device(inp)
-    prob = bslp.make_problem(w.dtype, w.hq, w.hkv, w.d, w.block, w.seqlens,
+    prob = bslp.make_problem(w.dtype, w.hq, w.hkv, w.d, w.block, w.query_lens,
                              softmax_scale=w.scale, q_scale=inp.q_scale, k_scale=inp.k_scale,
                              v_scale=inp.v_scale, page_table=table, page_size=w.page_size,
-                             kv_splits=kv_splits)
+                             kv_splits=kv_splits,
+                             kv_seqlens=w.seqlens if w.q_lens is not None else None)
     params = bslp.make_params(w.alpha if alpha is None else alpha, w.sink, w.window, w.recent,
                               w.correction if correction is None else correction)
     bufs = bslp.Buffers(prob)
@@ -105,9 +111,12 @@ class RequestView:
         start = sum(w.seqlens[:b])
         L = w.seqlens[b]
         self.L = L
+        qstart, Lq = sum(w.query_lens[:b]), w.query_lens[b]
+        self.q_off = L - Lq
+        self.qstart = qstart
         kk = inp.k_logical if inp.k_logical is not None else inp.k
         vv = inp.v_logical if inp.v_logical is not None else inp.v
-        self.q = dequant(inp.q[start:start + L], inp.q_scale, w.dtype)
+        self.q = dequant(inp.q[qstart:qstart + Lq], inp.q_scale, w.dtype)
         self._k = kk[start:start + L]
         self._v = vv[start:start + L]
         self.ks, self.vs = inp.k_scale, inp.v_scale
@@ -154,11 +163,9 @@ def compare(w: Workload, inp, g: GpuResult, tiles=None, alpha=None, correction=N
     rep = rep or Report()
     alpha = w.alpha if alpha is None else alpha
     corr = w.correction if correction is None else correction
-    segs = segments(w.seqlens, w.hkv, w.block)
+    segs = segments(w.seqlens, w.hkv, w.block, w.query_lens)
     views = {}
     pool_bases = np.concatenate([[0], np.cumsum([-(-L // w.block) for L in w.seqlens])])
-    starts = np.concatenate([[0], np.cumsum(w.seqlens)])
-    T = int(starts[-1])
     for (b, h, I, s, off) in segs:
         if tiles is not None and (b, h, I) not in tiles:
             continue
@@ -172,7 +179,7 @@ def compare(w: Workload, inp, g: GpuResult, tiles=None, alpha=None, correction=N
         rep.kbar_err = max(rep.kbar_err, float(np.abs(g.kbar[pb:pb + N, h] - kbar_h).max()),
                            float(np.abs(g.vbar[pb:pb + N, h] - vbar_h).max()))
         # scores
-        pos, heads, rows = oracle.tile_query_rows(rv.q, h, w.g, w.block, I)
+        pos, heads, rows = oracle.tile_query_rows(rv.q, h, w.g, w.block, I, rv.q_off)
         score = oracle.block_scores_row(rows, kbar_h, I, w.scale)
         sel_o, thresh = oracle.select_row(score, I, alpha, w.sink, w.window, w.recent)
         gs = g.scores[off:off + I + 1].astype(np.float64)
@@ -201,8 +208,8 @@ def compare(w: Workload, inp, g: GpuResult, tiles=None, alpha=None, correction=N
         todo = oracle.todo_row(sel_g, I, corr)
         O, lse = oracle.attend_rows(pos, rows, k_h, v_h, kbar_h, vbar_h, sel_g, todo, w.block,
                                     w.scale)
-        go = g.out[starts[b] + pos, heads]
-        gl = g.lse[heads, starts[b] + pos]
+        go = g.out[rv.qstart + pos - rv.q_off, heads]
+        gl = g.lse[heads, rv.qstart + pos - rv.q_off]
         rep.out_err = max(rep.out_err, float(np.abs(go - O).max()))
         fin = np.isfinite(lse)
         assert np.array_equal(fin, np.isfinite(gl)), f"LSE finiteness differs at {(b, h, I)}"
@@ -227,11 +234,15 @@ def sample_tiles(w: Workload, per_head: int = 4, heads=None, seed: int = 0):
     rng = np.random.default_rng(seed)
     heads = heads if heads is not None else sorted({0, w.hkv - 1})
     out = set()
-    for b, L in enumerate(w.seqlens):
+    for b, (L, Lq) in enumerate(zip(w.seqlens, w.query_lens)):
         N = -(-L // w.block)
+        if Lq == 0:
+            continue
+        i0 = (L - Lq) // w.block  # tiles that hold a query
+        span = N - i0
         for h in heads:
-            for I in {0, 1 % N, N // 2, N - 1, *rng.integers(0, N, per_head).tolist()}:
-                out.add((b, h, int(I)))
+            for I in {0, 1 % span, span // 2, span - 1, *rng.integers(0, span, per_head).tolist()}:
+                out.add((b, h, i0 + int(I)))
     return out
 
 

@@ -63,10 +63,21 @@ class Workload:
     vertical: int = 0
     page_size: int = 0  # 0: contiguous K/V
     seeds: tuple = (0,)
+    # queries per request when they are only the last positions of its keys
+    # (a chunk of a chunked prefill); None: every position is a query
+    q_lens: tuple | None = None
 
     @property
     def g(self) -> int:
         return self.hq // self.hkv
+
+    @property
+    def query_lens(self) -> tuple:
+        return tuple(self.q_lens) if self.q_lens is not None else tuple(self.seqlens)
+
+    @property
+    def total_queries(self) -> int:
+        return int(sum(self.query_lens))
 
     @property
     def total_tokens(self) -> int:
@@ -231,6 +242,10 @@ def make_inputs(w: Workload, seed: int, threads: int = 8) -> Inputs:
     import torch
 
     q, k, v = generate_f32(w, seed, threads)
+    if w.q_lens is not None:  # keep the queries of the last positions
+        starts = np.concatenate([[0], np.cumsum(w.seqlens)]).astype(np.int64)
+        q = np.concatenate([q[starts[b] + L - Lq:starts[b] + L]
+                            for b, (L, Lq) in enumerate(zip(w.seqlens, w.q_lens))])
     qs = ks = vs = 1.0
     if w.dtype == "f32":
         tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
