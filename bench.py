@@ -31,7 +31,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import (FP8_128K, GQA_BF16_16K, PAGED_VARLEN, SHARD_BF16_16K,  # noqa: E402
+from workloads import (CHUNK_BF16_64K, FP8_128K, GQA_BF16_16K, PAGED_VARLEN, SHARD_BF16_16K,  # noqa: E402
                        SWEEP_BF16_64K, TINY_F32, make_inputs)
 
 METRIC = "sparse prefill ms/layer + dense-equiv TFLOP/s at 64K/128K (MFMA % of peak)"
@@ -41,6 +41,7 @@ CONFIGS = {
     "16k-bf16": GQA_BF16_16K,
     "paged-varlen": PAGED_VARLEN,
     "16k-tp8-shard": SHARD_BF16_16K,
+    "64k-last-8k-chunk": CHUNK_BF16_64K,
     "tiny-f32": TINY_F32,
 }
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
@@ -78,8 +79,10 @@ def measured_traffic(workload: str):
 
 
 def dense_flops(w) -> float:
-    """QK^T + PV over the causal triangle, every query head."""
-    return 4.0 * w.d * w.hq * sum(L * (L + 1) / 2 for L in w.seqlens)
+    """QK^T + PV over the causal (query, key) pairs, every query head: query
+    position p sees keys 0..p, the queries being the last Lq of L positions."""
+    return 4.0 * w.d * w.hq * sum(L * (L + 1) / 2 - (L - Lq) * (L - Lq + 1) / 2
+                                  for L, Lq in zip(w.seqlens, w.query_lens))
 
 
 def effective_flops(w, cu: np.ndarray, idx: np.ndarray, correction: bool) -> tuple[float, float]:
@@ -90,21 +93,27 @@ def effective_flops(w, cu: np.ndarray, idx: np.ndarray, correction: bool) -> tup
     sel_total = 0
     causal_total = 0
     seg = 0
-    for L in w.seqlens:
+    for L, Lq in zip(w.seqlens, w.query_lens):
         N = -(-L // w.block)
+        qoff = L - Lq
+        i0 = qoff // w.block if Lq else N
+        n = N - i0  # tiles that hold a query
         for _h in range(w.hkv):
-            I = np.arange(N)
-            c = cu[seg + 1:seg + N + 1] - cu[seg:seg + N]
-            last = idx[cu[seg + 1:seg + N + 1] - 1]
+            I = np.arange(i0, N)
+            c = cu[seg + 1:seg + n + 1] - cu[seg:seg + n]
+            last = idx[np.maximum(cu[seg + 1:seg + n + 1] - 1, 0)]
             diag = (c > 0) & (last == I)
-            nb = np.minimum(w.block, L - I * w.block).astype(np.float64)
-            off = (c - diag).astype(np.float64)
-            exact = nb * w.block * off + np.where(diag, nb * (nb + 1) / 2, 0.0)
-            todo = (I - off) if correction else np.zeros(N)
-            pairs += float(np.sum(w.g * (exact + nb * todo)))
+            q0 = np.maximum(I * w.block, qoff)
+            nq = (np.minimum((I + 1) * w.block, L) - q0).astype(np.float64)
+            before = (c - diag).astype(np.float64)  # selected full blocks J < I
+            # row p of the diagonal block sees p - I*B + 1 of its keys
+            dpairs = nq * (q0 - I * w.block) + nq * (nq + 1) / 2
+            exact = nq * w.block * before + np.where(diag, dpairs, 0.0)
+            todo = (I - before) if correction else np.zeros(n)
+            pairs += float(np.sum(w.g * (exact + nq * todo)))
             sel_total += int(c.sum())
-            causal_total += N * (N + 1) // 2
-            seg += N
+            causal_total += int(np.sum(I + 1))
+            seg += n
     return 4.0 * w.d * pairs, sel_total / max(1, causal_total)
 
 
@@ -121,6 +130,7 @@ def cpu_baseline(w, inp, budget_s: float = 12.0) -> dict:
         return t.float().numpy().astype(np.float64)
 
     L = w.seqlens[0]
+    qoff = L - w.query_lens[0]
     N = -(-L // w.block)
     h = 0
     kk = inp.k_logical if inp.k_logical is not None else inp.k
@@ -133,13 +143,14 @@ def cpu_baseline(w, inp, budget_s: float = 12.0) -> dict:
     t_pool = time.time() - t0
     done = []
     elapsed = t_pool
-    for I in range(N - 1, -1, -1):
-        nb = min(w.block, L - I * w.block)
+    for I in range(N - 1, qoff // w.block - 1, -1):
+        q0 = max(I * w.block, qoff)
+        nb = min((I + 1) * w.block, L) - q0
         # the tile's own rows, indexed from 0; positions shifted back afterwards
-        q_tile = deq(inp.q[I * w.block:I * w.block + nb].contiguous(), inp.q_scale)
+        q_tile = deq(inp.q[q0 - qoff:q0 - qoff + nb].contiguous(), inp.q_scale)
         t1 = time.time()
         pos, heads, rows = oracle.tile_query_rows(q_tile, h, w.g, w.block, 0)
-        pos = pos + I * w.block
+        pos = pos + q0
         score = oracle.block_scores_row(rows, kbar, I, w.scale)
         sel, _ = oracle.select_row(score, I, w.alpha, w.sink, w.window, w.recent)
         todo = oracle.todo_row(sel, I, w.correction)
@@ -148,7 +159,8 @@ def cpu_baseline(w, inp, budget_s: float = 12.0) -> dict:
         done.append((I, nb))
         if elapsed > budget_s and len(done) >= 2:
             break
-    pairs = sum(w.g * (nb * I * w.block + nb * (nb + 1) / 2) for I, nb in done)
+    pairs = sum(w.g * (nb * (L - nb) + nb * (nb + 1) / 2) if I == N - 1 else
+                w.g * (nb * ((I + 1) * w.block - nb) + nb * (nb + 1) / 2) for I, nb in done)
     flops = 4.0 * w.d * pairs
     threads = os.cpu_count()
     try:
@@ -199,10 +211,11 @@ def main():
     dev = torch.device("cuda")
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     table = torch.from_numpy(inp.table).to(dev) if inp.table is not None else None
-    prob = bslp.make_problem(w.dtype, w.hq, w.hkv, w.d, w.block, w.seqlens,
+    prob = bslp.make_problem(w.dtype, w.hq, w.hkv, w.d, w.block, w.query_lens,
                              softmax_scale=w.scale, q_scale=inp.q_scale, k_scale=inp.k_scale,
                              v_scale=inp.v_scale, page_table=table, page_size=w.page_size,
-                             kv_splits=args.kv_splits)
+                             kv_splits=args.kv_splits,
+                             kv_seqlens=w.seqlens if w.q_lens is not None else None)
     params = bslp.make_params(w.alpha, w.sink, w.window, w.recent, w.correction)
     bufs = bslp.Buffers(prob)
     stream = torch.cuda.current_stream()
@@ -250,9 +263,9 @@ def main():
     esz = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
     T = w.total_tokens
     pooled = sum(-(-L // w.block) for L in w.seqlens)
-    score_elems = w.hkv * sum((-(-L // w.block)) * (-(-L // w.block) + 1) // 2 for L in w.seqlens)
-    s1_bytes = (T * w.hq * w.d * esz + 2 * T * w.hkv * w.d * esz + 2 * pooled * w.hkv * w.d * 4
-                + score_elems * 4)
+    score_elems = int(bufs.sizes.score_elems)
+    s1_bytes = (w.total_queries * w.hq * w.d * esz + 2 * T * w.hkv * w.d * esz
+                + 2 * pooled * w.hkv * w.d * 4 + score_elems * 4)
 
     res = {
         "metric": METRIC,
@@ -268,7 +281,8 @@ def main():
         "dtype": cdt,
         "data": "synthetic (seeded planted-block generator)",
         "config": {
-            "workload": w.name, "seqlens": list(w.seqlens), "hq": w.hq, "hkv": w.hkv,
+            "workload": w.name, "seqlens": list(w.seqlens), "query_lens": list(w.query_lens),
+            "hq": w.hq, "hkv": w.hkv,
             "input_dtype": w.dtype, "head_dim": w.d, "block": w.block, "alpha": w.alpha, "sink_blocks": w.sink,
             "window_blocks": w.window, "recent_blocks": w.recent,
             "mean_correction": bool(w.correction), "page_size": w.page_size,

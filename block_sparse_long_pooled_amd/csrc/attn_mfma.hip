@@ -575,7 +575,7 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
   }
 }
 
-template <int DT, int D, int NW, int RT>
+template <int DT, int D, int NW, int RT, bool PERSIST>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     Plan p, KVDesc kv, const void* __restrict__ q, const void* __restrict__ k,
     const void* __restrict__ v, const uint16_t* __restrict__ kb2,
@@ -768,7 +768,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   }
   };
 
-  if (items == nullptr) {
+  if constexpr (!PERSIST) {
     // one workgroup per unit, enumerated heaviest first: longest request
     // first, tiles in descending I, then row block, KV head innermost
     const int64_t unit = blockIdx.x;
@@ -779,8 +779,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const int per_I = p.hkv * units_per_seg;
     const int rem = (int)(local % per_I);
     run_unit(b, p.seq[b].nblk - 1 - (int)(local / per_I), rem % p.hkv, rem / p.hkv, 0);
-    return;
-  }
+  } else {
   // split launch: persistent workgroups take items from the list the
   // preparation kernel wrote (heaviest segments first) until it is empty
   const int n_items = queue[1];
@@ -798,7 +797,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     segment_tile(p.seq[b], (int)(seg - p.seq[b].seg_base), h, I);
     run_unit(b, I, h, (code >> 4) & 15, code & 15);
   }
-
+  }
 }
 
 // Merge of the KV splits of the rows of every split segment: with M =
@@ -1027,7 +1026,7 @@ static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs&
   const int splits = a.splits;
   const int corr = a.correction && !a.dense;
   if (splits == 1) {
-    hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT>), dim3((unsigned)base), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT, false>), dim3((unsigned)base), dim3(NW * 64), 0,
                        st, pl, kv, a.q, a.k, a.v, (const uint16_t*)kb2, (const uint16_t*)vb16,
                        a.cu, a.idx, c, a.v_scale, corr, a.dense, units_per_seg, 1,
                        (uint16_t*)a.out, a.lse, nullptr, nullptr, nullptr, nullptr);
@@ -1047,10 +1046,10 @@ static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs&
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(&attn_mfma_kernel<DT, D, NW, RT>), NW * 64, 0);
+        &per_cu, reinterpret_cast<const void*>(&attn_mfma_kernel<DT, D, NW, RT, true>), NW * 64, 0);
   if (e != hipSuccess) return e;
   const int64_t grid = std::min<int64_t>(split_items(p, splits), (int64_t)cus * std::max(1, per_cu));
-  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      st, pl, kv, a.q, a.k, a.v, (const uint16_t*)kb2, (const uint16_t*)vb16,
                      a.cu, a.idx, c, a.v_scale, corr, a.dense, units_per_seg, splits,
                      (uint16_t*)a.out, a.lse, part_o, part_ml, items, queue);

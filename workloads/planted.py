@@ -109,6 +109,9 @@ PAGED_VARLEN = Workload("paged-varlen-6req-bf16-hq32-hkv8",
 # units, the case KV splitting is for.
 SHARD_BF16_16K = Workload("tp8-shard-bf16-L16384-hq4-hkv1", (16384,), 4, 1, 128, 128, "bf16",
                           attractors=4, vertical=8)
+# The last 8K-token chunk of a chunked 64K prefill: 8K queries over 64K keys.
+CHUNK_BF16_64K = Workload("chunk8k-of-64k-bf16-hq32-hkv8", (65536,), 32, 8, 128, 128, "bf16",
+                          q_lens=(8192,))
 SWEEP_ALPHAS = (0.2, 0.1, 0.05, 0.025, 0.0125)
 
 
