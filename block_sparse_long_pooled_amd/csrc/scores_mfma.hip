@@ -204,28 +204,39 @@ __global__ __launch_bounds__(NW * 64) void scores_mfma_kernel(Plan p,
             acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t][ks], bop, acc[t], 0, 0, 0);
         }
       }
+      // max and sum of exp2(c2 * acc) over the wave's rows of block J; the
+      // maximum is taken on the raw products (c2 > 0) and the scale enters
+      // the exponent's FMA.  Only the chunk past the last block and the row
+      // tile past the last row need masks (a uniform test per wave).
       const int J = c * kChunk + jj;
-      const bool okJ = J < nJ;
       float mx = -INFINITY;
+      if (row0 + RT * 32 <= R && (c + 1) * kChunk <= nJ) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
+        for (int t = 0; t < RT; ++t) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = row0 + t * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          const float x = (okJ && r < R) ? acc[t][i] * c2 : -INFINITY;
-          acc[t][i] = x;
-          mx = fmaxf(mx, x);
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[t][i]);
+        }
+      } else {
+        const bool okJ = J < nJ;
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = row0 + t * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            acc[t][i] = (okJ && r < R) ? acc[t][i] : -INFINITY;
+            mx = fmaxf(mx, acc[t][i]);
+          }
         }
       }
       mx = pair_max(mx);
-      const float mu = mx == -INFINITY ? 0.f : mx;
+      const float nmu = mx == -INFINITY ? 0.f : -mx * c2;
       float sum = 0.f;
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(acc[t][i] - mu);
+        for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(fmaf(acc[t][i], c2, nmu));
       }
-      pm = mx;
+      pm = mx == -INFINITY ? -INFINITY : mx * c2;
       ps = pair_sum(sum);
     }
     if (half == 0) {
