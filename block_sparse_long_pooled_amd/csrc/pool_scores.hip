@@ -7,46 +7,67 @@
 namespace bslp {
 
 // ------------------------------------------------------------------ pooling
-// One workgroup per (pooled row, KV head, K-or-V).  Threads split the block's
-// rows into RG interleaved groups; each thread sums one column of its group's
-// rows (consecutive threads read consecutive columns of a token row), and the
-// groups are combined in fixed order, so results are deterministic.
+// One workgroup per (pooled row, group of HC KV heads, K-or-V): a token row
+// of HC heads is HC*D contiguous elements, read by TPR = HC*D/8 threads with
+// one 8-element (16-byte for bf16) load each, so every load instruction of a
+// wave covers a contiguous 1 KB.  The RG = 256/TPR row groups take the
+// block's rows r, r + RG, ...; each thread sums its 8 columns over its rows,
+// and the groups are combined in fixed order, so results are deterministic.
+// HBM-bound: the block's K (or V) rows are read once.
+constexpr int kPoolThreads = 256;
+
+template <int D>
+constexpr int pool_heads() { return kPoolThreads * 8 / D; }  // heads per workgroup
+
 template <int DT, int D>
-__global__ __launch_bounds__(256) void pool_kernel(Plan p, KVDesc kv,
-                                                   const typename Elem<DT>::T* __restrict__ k,
-                                                   const typename Elem<DT>::T* __restrict__ v,
-                                                   float k_scale, float v_scale,
-                                                   float* __restrict__ kbar,
-                                                   float* __restrict__ vbar) {
-  constexpr int RG = 256 / D;
-  __shared__ float part[RG][D];
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(Plan p, KVDesc kv,
+                                                            const typename Elem<DT>::T* __restrict__ k,
+                                                            const typename Elem<DT>::T* __restrict__ v,
+                                                            float k_scale, float v_scale,
+                                                            float* __restrict__ kbar,
+                                                            float* __restrict__ vbar) {
+  __shared__ __attribute__((aligned(16))) float part[kPoolThreads * 8];
   const int prow = blockIdx.x;
-  const int h = blockIdx.y;
+  const int h0 = blockIdx.y * pool_heads<D>();
   const bool is_v = blockIdx.z != 0;
+  const int hc = min(pool_heads<D>(), p.hkv - h0);
+  const int tpr = hc * D / 8;          // threads per token row (D % 8 == 0)
+  const int rg_n = kPoolThreads / tpr; // row groups
+  const int tid = threadIdx.x;
+  const int rg = tid / tpr, col8 = tid % tpr;
+  const bool active = rg < rg_n;
   int b = 0;
   while (b + 1 < p.num_seqs && p.seq[b + 1].pool_base <= prow) ++b;
   const SeqInfo s = p.seq[b];
   const int J = prow - s.pool_base;
   const int j0 = J * p.B;
   const int cnt = min(p.B, s.len - j0);
-  const int col = threadIdx.x % D;
-  const int rg = threadIdx.x / D;
   const typename Elem<DT>::T* x = is_v ? v : k;
-  float acc = 0.f;
-  for (int r = rg; r < cnt; r += RG) {
-    const int64_t row = kv.row(b, s.kv_start, j0 + r);
-    acc += Elem<DT>::load(x, (row * p.hkv + h) * D + col);
-  }
-  part[rg][col] = acc;
-  __syncthreads();
-  if (rg == 0) {
-    float t = part[0][col];
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    for (int r = rg; r < cnt; r += rg_n) {
+      const int64_t row = kv.row(b, s.kv_start, j0 + r);
+      float e[8];
+      load8<DT>(x, (row * p.hkv + h0) * D + col8 * 8, e);
 #pragma unroll
-    for (int g2 = 1; g2 < RG; ++g2) t += part[g2][col];
+      for (int i = 0; i < 8; ++i) acc[i] += e[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[rg * tpr * 8 + col8 * 8 + i] = acc[i];
+  }
+  __syncthreads();
+  if (tid < tpr) {
     const float sc = p.dscale ? p.dscale[is_v ? 2 : 1] : (is_v ? v_scale : k_scale);
-    const float mean = t / (float)cnt * sc;
-    float* out = is_v ? vbar : kbar;
-    out[((int64_t)prow * p.hkv + h) * D + col] = mean;
+    float* out = (is_v ? vbar : kbar) + ((int64_t)prow * p.hkv + h0) * D + tid * 8;
+    float m[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float t = part[tid * 8 + i];
+      for (int g2 = 1; g2 < rg_n; ++g2) t += part[g2 * tpr * 8 + tid * 8 + i];
+      m[i] = t / (float)cnt * sc;
+    }
+    *reinterpret_cast<float4*>(out) = make_float4(m[0], m[1], m[2], m[3]);
+    *reinterpret_cast<float4*>(out + 4) = make_float4(m[4], m[5], m[6], m[7]);
   }
 }
 
@@ -187,8 +208,9 @@ static hipError_t launch_stage1_t(const Plan& p, const KVDesc& kv, const void* q
                                   hipStream_t st) {
   using T = typename Elem<DT>::T;
   if (p.pooled_rows > 0) {
-    dim3 grid((unsigned)p.pooled_rows, (unsigned)p.hkv, 2);
-    hipLaunchKernelGGL((pool_kernel<DT, D>), grid, dim3(256), 0, st, p, kv, (const T*)k,
+    const int groups = (p.hkv + pool_heads<D>() - 1) / pool_heads<D>();
+    dim3 grid((unsigned)p.pooled_rows, (unsigned)groups, 2);
+    hipLaunchKernelGGL((pool_kernel<DT, D>), grid, dim3(kPoolThreads), 0, st, p, kv, (const T*)k,
                        (const T*)v, k_scale, v_scale, kbar, vbar);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
