@@ -55,6 +55,12 @@ SMALL = [
              alpha=0.3),
     Workload("wide-forced", (1536,), 4, 2, 128, 64, "bf16", sink=3, window=4, recent=2,
              alpha=0.5),
+    # more KV heads than one pooling workgroup covers (16 at d = 128, 32 at
+    # d = 64): head groups of 16 + 4 and 32 + 8
+    Workload("kv-heads-20-d128", (600,), 20, 20, 128, 64, "bf16", attractors=4),
+    Workload("kv-heads-40-d64-fp8", (333,), 40, 40, 64, 64, "fp8", sigma_c=1.5),
+    # 17 heads of 64 dims: 136 threads per token row, one row group
+    Workload("kv-heads-17-d64-f32", (200,), 17, 17, 64, 64, "f32"),
 ]
 
 
