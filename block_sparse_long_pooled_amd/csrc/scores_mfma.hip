@@ -17,8 +17,8 @@
 // are accumulated lo first, then mid, then hi, so only the last eight
 // accumulations run at the magnitude of the logit.
 //
-// Work layout.  One workgroup per segment, NW waves; wave w owns RT row tiles
-// of 32 packed rows (Q in registers as the A operand of
+// Work layout.  One workgroup per segment, NW waves (up to 16); wave w owns
+// RT row tiles of 32 packed rows (Q in registers as the A operand of
 // v_mfma_f32_32x32x16_bf16).  Key blocks are processed in chunks of 32: the
 // chunk's split kbar rows are staged in LDS (double buffered, next chunk
 // prefetched into registers while the current one is multiplied) and read
@@ -86,8 +86,12 @@ __device__ __forceinline__ uint4 load_q8_bf16(const typename Elem<DT>::T* p, int
 
 }  // namespace
 
+// Two row tiles per wave at 16 waves (1024-row tiles) or at 8 waves for bf16
+// fit in 128 VGPRs, i.e. 4 waves per SIMD: two 8-wave workgroups share a CU,
+// so one workgroup's per-chunk barrier and combine overlap the other's MFMAs.
 template <int DT, int D, int RT, int NW>
-__global__ __launch_bounds__(NW * 64) void scores_mfma_kernel(Plan p,
+__global__ __launch_bounds__(NW * 64, (RT == 2 && (NW == 16 || (DT == kBF16 && NW == 8))) ? 4 : 1)
+void scores_mfma_kernel(Plan p,
                                                               const typename Elem<DT>::T* __restrict__ q,
                                                               const float* __restrict__ kbar,
                                                               float c2, float* __restrict__ scores) {
@@ -310,7 +314,7 @@ static hipError_t launch_scores_d(const Plan& p, const void* q, const float* kba
   if (rmax <= 128) return launch_scores_t<DT, D, 1, 4>(p, q, kbar, c2, scores, st);
   if (rmax <= 256) return launch_scores_t<DT, D, 2, 4>(p, q, kbar, c2, scores, st);
   if (rmax <= 512) return launch_scores_t<DT, D, 2, 8>(p, q, kbar, c2, scores, st);
-  return launch_scores_t<DT, D, 4, 8>(p, q, kbar, c2, scores, st);
+  return launch_scores_t<DT, D, 2, 16>(p, q, kbar, c2, scores, st);
 }
 
 bool scores_mfma_supported(const Plan& p, int dtype) {
