@@ -196,8 +196,9 @@ def main():
                     help="timed calls of the dense causal path (0 skips it)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the operator has no "
-              "cross-GPU step and this build runs on a single MI355X.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the layer has no "
+              "cross-GPU step; across GPUs it shards by KV head or by request with no exchange.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

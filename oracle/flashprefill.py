@@ -14,7 +14,7 @@ Sources, cited by page title and section:
   [PRR] the PRR (Predict, Reuse, Repair) review page, Sec. 4.3, Eq. 6: the
         online-softmax merge recurrence.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * logits carry the softmax scale in scoring and in attention;
   * scoring is block-causal (J <= I) with no token mask inside the diagonal
     block;
