@@ -192,6 +192,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--kv-splits", type=int, default=0,
                     help="attention KV splits: 0 automatic, 1 none, 2..16 forced")
+    ap.add_argument("--quant-reps", type=int, default=5,
+                    help="timed online e4m3 quantisations of Q for bf16 workloads (0 skips)")
     ap.add_argument("--dense-reps", type=int, default=3,
                     help="timed calls of the dense causal path (0 skips it)")
     args = ap.parse_args()
@@ -324,6 +326,25 @@ def main():
         res["dense_attention"] = {"ms": dense_ms, "tflops": dense_tf, "frac": dense_tf / peak,
                                   "sparse_layer_speedup": dense_ms / ms_step}
         del dout, dlse
+    if args.quant_reps > 0 and q.dtype == torch.bfloat16:
+        # online per-tensor e4m3 quantisation of the workload's Q: amax pass,
+        # then codes; 5 bytes per element (two reads of 2, one write of 1)
+        codes = torch.empty(q.numel(), dtype=torch.uint8, device=dev)
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+        qflat = q.reshape(-1)
+        bslp.quantize_e4m3(qflat, codes, scale, sp)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.quant_reps):
+            bslp.quantize_e4m3(qflat, codes, scale, sp)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        qms = d0.elapsed_time(d1) / args.quant_reps
+        gbs = 5.0 * q.numel() / (qms * 1e-3) / 1e9
+        res["online_fp8_quant_q"] = {"elements": q.numel(), "ms": qms, "gbs": gbs,
+                                     "frac_of_8TBs": gbs / PEAK_HBM_GBS}
+        del codes, scale
     if args.copy_calibration:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
