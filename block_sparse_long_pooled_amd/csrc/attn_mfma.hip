@@ -15,11 +15,11 @@
 //
 // Pipeline.  The unit's work is a uniform sequence of 64-key steps: the
 // selected blocks from the CSR list walked backwards (B/64 steps each), then
-// the correction chunks of 32 pooled blocks that hold at least one block of
+// the correction chunks of 64 pooled blocks that hold at least one block of
 // todo = valid & ~selected (valid = J <= I-1, fully visible to the tile).
-// A correction step's 64 keys are the 32 pooled means as bf16 pairs hi + lo
-// (the float32 mean to within 2^-18 of itself): keys 0-31 hold hi, keys
-// 32-63 lo, and the two score halves are added before the softmax, so the
+// A correction step's 64 keys are 64 pooled means as bf16 pairs hi + lo
+// (the float32 mean to within 2^-18 of itself), hi in the K buffer and lo in
+// a second one; both products accumulate into the same scores, so the
 // pooled logits carry no bf16 rounding.
 // Every thread derives the same sequence, so no step needs a vote.  After
 // the step's barrier each wave writes the prefetched step n+1 into the other
@@ -57,7 +57,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16 bytes, kept
 namespace {
 
 constexpr int kKeys = 64;      // keys per pipeline step
-constexpr int kCorrRows = 32;  // pooled blocks per correction step (hi + lo keys)
+constexpr int kCorrRows = 64;  // pooled blocks per correction step (hi and lo K rows)
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum StepKind : int { kExact = 0, kCorr = 1, kDone = 2 };
@@ -109,7 +109,7 @@ struct Step {
   int kind;  // StepKind
   int t;     // exact: CSR position
   int hf;    // exact: 64-key half of the block
-  int c;     // correction: chunk of 32 pooled blocks
+  int c;     // correction: chunk of 64 pooled blocks
   int J;     // exact: block index idx[t]
   int Jn;    // exact: idx[t-1], loaded one block ahead so no step waits on it
 };
@@ -137,7 +137,7 @@ struct UnitCtx {
 // result.  The attention and the merge kernel evaluate it alike.
 __device__ __forceinline__ int segment_splits(int n_sel, int I, int B, int correction,
                                               int splits) {
-  const int steps = n_sel * (B / 64) + (correction && I > 0 ? (I + 31) / 32 : 0);
+  const int steps = n_sel * (B / 64) + (correction && I > 0 ? (I + kCorrRows - 1) / kCorrRows : 0);
   return max(1, min(splits, steps / 24));
 }
 
@@ -146,12 +146,14 @@ __device__ __forceinline__ int block_at(const int32_t* idx, int t, const UnitCtx
   return u.dense ? t : idx[t];
 }
 
-// todo bits of correction chunk c (blocks 32c .. 32c+31, valid J <= I-1).
+// todo bits of correction chunk c (blocks 64c .. 64c+63, valid J <= I-1).
 __device__ __forceinline__ uint64_t chunk_todo(const uint32_t* selbits, int c, int I) {
   const int nv = min(max(I - kCorrRows * c, 0), kCorrRows);
   if (nv == 0) return 0;
-  const uint32_t m = nv >= 32 ? 0xffffffffu : ((1u << nv) - 1u);
-  return (uint32_t)uni((int)(~selbits[c] & m));
+  const uint64_t m = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
+  const uint64_t t = ~((uint64_t)selbits[2 * c] | ((uint64_t)selbits[2 * c + 1] << 32)) & m;
+  return (uint64_t)(uint32_t)uni((int)(uint32_t)t) |
+         ((uint64_t)(uint32_t)uni((int)(uint32_t)(t >> 32)) << 32);
 }
 
 __device__ __forceinline__ void find_chunk(Step& st, const uint32_t* selbits, int I, int cstep) {
@@ -225,6 +227,7 @@ struct AttnCfg {
 template <int D, int NW, int RT>
 struct Prefetch {
   u32x4_t k[AttnCfg<D, NW, RT>::KL];
+  u32x4_t kl[AttnCfg<D, NW, RT>::KL];  // correction steps: the lo rows of K
   u32x4_t v0[AttnCfg<D, NW, RT>::VL];  // key 2a of the pair
   u32x4_t v1[AttnCfg<D, NW, RT>::VL];  // key 2a + 1
 };
@@ -269,12 +272,13 @@ __device__ __forceinline__ const char* uniform_ptr(const void* p) {
   return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
 }
 
-// Offsets of the K pieces of a correction step: key r < 32 is the hi row of
-// pooled block r, key 32 + r its lo row, from the [pooled row, {hi, lo}, Hkv,
-// D] bf16 layout.
+// Offsets of the K pieces of a correction step: key r is pooled block r, its
+// hi row for the K buffer and its lo row for the second one, from the [pooled
+// row, {hi, lo}, Hkv, D] bf16 layout.
 template <int D, int NW, int RT>
 struct CorrOffsets {
-  uint32_t k[AttnCfg<D, NW, RT>::KL];
+  uint32_t k[AttnCfg<D, NW, RT>::KL];   // hi rows
+  uint32_t kl[AttnCfg<D, NW, RT>::KL];  // lo rows
 };
 
 template <int D, int NW, int RT>
@@ -287,8 +291,8 @@ __device__ __forceinline__ CorrOffsets<D, NW, RT> corr_offsets(int hkv) {
   for (int i = 0; i < C::KL; ++i) {
     const int f = min(tid + i * C::NT, C::KUN - 1);
     const int key = f / C::KU;
-    o.k[i] = (uint32_t)(2 * (key % kCorrRows) + key / kCorrRows) * row_bytes +
-             (uint32_t)(f % C::KU) * 16;
+    o.k[i] = (uint32_t)(2 * key) * row_bytes + (uint32_t)(f % C::KU) * 16;
+    o.kl[i] = (uint32_t)(2 * key + 1) * row_bytes + (uint32_t)(f % C::KU) * 16;
   }
   return o;
 }
@@ -296,13 +300,12 @@ __device__ __forceinline__ CorrOffsets<D, NW, RT> corr_offsets(int hkv) {
 // Global -> registers for one step.  Exact steps read tokens key0.. of the
 // request (through the page table when K/V are paged), as bf16 or as e4m3
 // codes (8 bytes per piece, widened when written to LDS); correction steps
-// read the bf16 hi/lo rows of 32 pooled keys and their 32 pooled values.
+// read the bf16 hi and lo rows of 64 pooled keys and their 64 pooled values.
 // When the step's rows are consecutive in memory (contiguous K/V, pages of at
 // least 64 tokens, pooled rows) the loads are raw buffer loads from one
 // scalar descriptor plus the fixed per-thread offsets; the descriptor ends
 // after the step's last valid row, so rows past it (the short last block, the
-// last correction chunk, the value rows of keys 32-63 of a correction step)
-// read as zero.  With smaller pages every key's row is resolved on its own
+// last correction chunk) read as zero.  With smaller pages every key's row is resolved on its own
 // and keys past the end re-read the last valid row.  Either way those keys'
 // scores are masked.
 template <int DT, int D, int NW, int RT>
@@ -367,6 +370,11 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
       for (int i = 0; i < C::KL; ++i)
         pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(exact ? off16.k[i] : offc.k[i]),
                                                         0, 0);
+      if (!exact) {
+#pragma unroll
+        for (int i = 0; i < C::KL; ++i)
+          pf.kl[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)offc.kl[i], 0, 0);
+      }
 #pragma unroll
       for (int i = 0; i < C::VL; ++i) {
         pf.v0[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off16.v0[i], 0, 0);
@@ -421,8 +429,8 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
 // Registers -> LDS: K row-major, V transposed with permuted key columns; both
 // with padded rows so the 16-byte operand reads of 16 lanes hit distinct banks.
 template <int D, int NW, int RT>
-__device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, bool widen,
-                                           uint16_t* Ks, uint16_t* Vt) {
+__device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, bool widen, bool corr,
+                                           uint16_t* Ks, uint16_t* Kl, uint16_t* Vt) {
   using C = AttnCfg<D, NW, RT>;
   const int tid = threadIdx.x;
 #pragma unroll
@@ -432,6 +440,7 @@ __device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, bool w
     const int key = f / C::KU, un = f % C::KU;
     *reinterpret_cast<u32x4_t*>(Ks + key * C::KLD + un * 8) =
         widen ? e4m3x8_to_bf16x8(pf.k[i][0], pf.k[i][1]) : pf.k[i];
+    if (corr) *reinterpret_cast<u32x4_t*>(Kl + key * C::KLD + un * 8) = pf.kl[i];
   }
 #pragma unroll
   for (int i = 0; i < C::VL; ++i) {
@@ -457,7 +466,8 @@ enum Mode : int { kPlain = 0, kDiag = 1, kCorrMode = 2 };
 // One 64-key step of one wave over its RT row tiles: S^T = K Q^T, online
 // softmax, O^T += V^T P^T.  `mode` is uniform across the workgroup.
 template <int D, int NW, int RT>
-__device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t* Vt,
+__device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t* Kl,
+                                             const uint16_t* Vt,
                                              const bf16x8_t (&qf)[RT][D / 16],
                                              f32x16_t (&oacc)[RT][D / 32], float (&m_run)[RT],
                                              float (&l_run)[RT], float c, int mode, int key0,
@@ -475,29 +485,28 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
       for (int r = 0; r < 16; ++r) sacc[rt][kt][r] = 0.f;
     }
   }
-  const uint16_t* kbase = Ks + key_l * C::KLD + half * 8;
+  auto qk = [&](const uint16_t* Kb) __attribute__((always_inline)) {
+    const uint16_t* kbase = Kb + key_l * C::KLD + half * 8;
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
+    for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const bf16x8_t a =
-          *reinterpret_cast<const bf16x8_t*>(kbase + kt * 32 * C::KLD + ks * 16);
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8_t a =
+            *reinterpret_cast<const bf16x8_t*>(kbase + kt * 32 * C::KLD + ks * 16);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        sacc[rt][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rt][ks], sacc[rt][kt], 0, 0, 0);
+        for (int rt = 0; rt < RT; ++rt)
+          sacc[rt][kt] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rt][ks], sacc[rt][kt], 0, 0, 0);
+      }
     }
-  }
+  };
+  // a correction step's pooled logits: the lo rows' products first (the
+  // small terms), then the hi rows', into the same accumulators
+  if (mode == kCorrMode) qk(Kl);
+  qk(Ks);
   // masks: diagonal block (token causality and the request end) or the
   // correction chunk's todo bits; branch-free per element, uniform per step
   if (mode != kPlain) {
-    if (mode == kCorrMode) {
-      // pooled logits: hi keys 0-31 plus lo keys 32-63 (masked below)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[rt][0][r] += sacc[rt][1][r];
-      }
-    }
     uint64_t bits;
     if (mode == kDiag) {
       const int nvis = len - key0;  // >= 1
@@ -591,6 +600,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   }
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKeys * C::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Kl[2][kKeys * C::KLD];  // correction lo rows
   __shared__ uint32_t selbits[kMaxBlocksPerSeq / 32];
   __shared__ int next_item;
 
@@ -678,7 +688,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   Step cur = first_step(u, idx, selbits, correction);
   if (cur.kind != kDone) {
     fetch_step<DT, D, NW, RT>(pf, off16, off8, offc, cur, u, kv, p.hkv, k, v, kb2, vb16);
-    store_step<D, NW, RT>(pf, DT == kFP8 && cur.kind == kExact, Ks[0], Vt[0]);
+    store_step<D, NW, RT>(pf, DT == kFP8 && cur.kind == kExact, cur.kind == kCorr, Ks[0], Kl[0],
+                          Vt[0]);
   }
   uniform(cur);
   // the query rows and the first step have arrived; saying so here keeps the
@@ -703,7 +714,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
       uniform(nn);
     }
     if (nxt.kind != kDone)
-      store_step<D, NW, RT>(pf, DT == kFP8 && nxt.kind == kExact, Ks[buf ^ 1], Vt[buf ^ 1]);
+      store_step<D, NW, RT>(pf, DT == kFP8 && nxt.kind == kExact, nxt.kind == kCorr, Ks[buf ^ 1],
+                            Kl[buf ^ 1], Vt[buf ^ 1]);
     if (nn.kind != kDone) fetch_step<DT, D, NW, RT>(pf, off16, off8, offc, nn, u, kv, p.hkv, k, v, kb2, vb16);
     if (wave_active) {
       int mode, key0 = 0;
@@ -715,7 +727,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
         mode = kCorrMode;
         todo = chunk_todo(selbits, cur.c, I);
       }
-      compute_step<D, NW, RT>(Ks[buf], Vt[buf], qf, oacc, m_run, l_run, c, mode, key0, s.len,
+      compute_step<D, NW, RT>(Ks[buf], Kl[buf], Vt[buf], qf, oacc, m_run, l_run, c, mode, key0, s.len,
                               qpos, todo, bias);
     }
     cur = nxt;
