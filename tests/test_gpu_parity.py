@@ -61,6 +61,10 @@ SMALL = [
     Workload("kv-heads-40-d64-fp8", (333,), 40, 40, 64, 64, "fp8", sigma_c=1.5),
     # 17 heads of 64 dims: 136 threads per token row, one row group
     Workload("kv-heads-17-d64-f32", (200,), 17, 17, 64, 64, "f32"),
+    # 129 blocks: tiles I = 0..128 cover one, two and three correction chunks
+    # of 64 pooled blocks, the last with a single block
+    Workload("corr-chunks-129-blocks", (8200,), 4, 1, 64, 64, "bf16", attractors=4),
+    Workload("corr-chunks-fp8", (8200,), 8, 1, 64, 64, "fp8", sigma_c=1.5),
 ]
 
 
