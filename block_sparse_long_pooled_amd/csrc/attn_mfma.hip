@@ -308,7 +308,7 @@ __device__ __forceinline__ CorrOffsets<D, NW, RT> corr_offsets(int hkv) {
 // last correction chunk) read as zero.  With smaller pages every key's row is resolved on its own
 // and keys past the end re-read the last valid row.  Either way those keys'
 // scores are masked.
-template <int DT, int D, int NW, int RT>
+template <int DT, int D, int NW, int RT, bool CORR>
 __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
                                            const FetchOffsets<D, NW, RT>& off16,
                                            const FetchOffsets<D, NW, RT>& off8,
@@ -370,7 +370,7 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
       for (int i = 0; i < C::KL; ++i)
         pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(exact ? off16.k[i] : offc.k[i]),
                                                         0, 0);
-      if (!exact) {
+      if (CORR && !exact) {
 #pragma unroll
         for (int i = 0; i < C::KL; ++i)
           pf.kl[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)offc.kl[i], 0, 0);
@@ -428,7 +428,7 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
 
 // Registers -> LDS: K row-major, V transposed with permuted key columns; both
 // with padded rows so the 16-byte operand reads of 16 lanes hit distinct banks.
-template <int D, int NW, int RT>
+template <int D, int NW, int RT, bool CORR>
 __device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, bool widen, bool corr,
                                            uint16_t* Ks, uint16_t* Kl, uint16_t* Vt) {
   using C = AttnCfg<D, NW, RT>;
@@ -440,7 +440,7 @@ __device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, bool w
     const int key = f / C::KU, un = f % C::KU;
     *reinterpret_cast<u32x4_t*>(Ks + key * C::KLD + un * 8) =
         widen ? e4m3x8_to_bf16x8(pf.k[i][0], pf.k[i][1]) : pf.k[i];
-    if (corr) *reinterpret_cast<u32x4_t*>(Kl + key * C::KLD + un * 8) = pf.kl[i];
+    if (CORR && corr) *reinterpret_cast<u32x4_t*>(Kl + key * C::KLD + un * 8) = pf.kl[i];
   }
 #pragma unroll
   for (int i = 0; i < C::VL; ++i) {
@@ -465,7 +465,7 @@ enum Mode : int { kPlain = 0, kDiag = 1, kCorrMode = 2 };
 
 // One 64-key step of one wave over its RT row tiles: S^T = K Q^T, online
 // softmax, O^T += V^T P^T.  `mode` is uniform across the workgroup.
-template <int D, int NW, int RT>
+template <int D, int NW, int RT, bool CORR>
 __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t* Kl,
                                              const uint16_t* Vt,
                                              const bf16x8_t (&qf)[RT][D / 16],
@@ -502,7 +502,7 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
   };
   // a correction step's pooled logits: the lo rows' products first (the
   // small terms), then the hi rows', into the same accumulators
-  if (mode == kCorrMode) qk(Kl);
+  if (CORR && mode == kCorrMode) qk(Kl);
   qk(Ks);
   // masks: diagonal block (token causality and the request end) or the
   // correction chunk's todo bits; branch-free per element, uniform per step
@@ -584,7 +584,7 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
   }
 }
 
-template <int DT, int D, int NW, int RT, bool PERSIST>
+template <int DT, int D, int NW, int RT, bool PERSIST, bool CORR>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     Plan p, KVDesc kv, const void* __restrict__ q, const void* __restrict__ k,
     const void* __restrict__ v, const uint16_t* __restrict__ kb2,
@@ -594,13 +594,15 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ items,
     int* __restrict__ queue) {
   using C = AttnCfg<D, NW, RT>;
+  if constexpr (!CORR) correction = 0;  // compiled without correction steps
   if (p.dscale) {  // fp8 scales kept on the device
     c *= p.dscale[0] * p.dscale[1];
     out_scale = p.dscale[2];
   }
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKeys * C::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Kl[2][kKeys * C::KLD];  // correction lo rows
+  // correction steps: the lo rows of the pooled keys (a stub without them)
+  __shared__ __attribute__((aligned(16))) uint16_t Kl[2][CORR ? kKeys * C::KLD : 8];
   __shared__ uint32_t selbits[kMaxBlocksPerSeq / 32];
   __shared__ int next_item;
 
@@ -687,8 +689,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   Prefetch<D, NW, RT> pf;
   Step cur = first_step(u, idx, selbits, correction);
   if (cur.kind != kDone) {
-    fetch_step<DT, D, NW, RT>(pf, off16, off8, offc, cur, u, kv, p.hkv, k, v, kb2, vb16);
-    store_step<D, NW, RT>(pf, DT == kFP8 && cur.kind == kExact, cur.kind == kCorr, Ks[0], Kl[0],
+    fetch_step<DT, D, NW, RT, CORR>(pf, off16, off8, offc, cur, u, kv, p.hkv, k, v, kb2, vb16);
+    store_step<D, NW, RT, CORR>(pf, DT == kFP8 && cur.kind == kExact, cur.kind == kCorr, Ks[0], Kl[0],
                           Vt[0]);
   }
   uniform(cur);
@@ -698,7 +700,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   Step nxt = cur;
   if (cur.kind != kDone) advance(nxt, u, idx, selbits, correction);
   uniform(nxt);
-  if (nxt.kind != kDone) fetch_step<DT, D, NW, RT>(pf, off16, off8, offc, nxt, u, kv, p.hkv, k, v, kb2, vb16);
+  if (nxt.kind != kDone) fetch_step<DT, D, NW, RT, CORR>(pf, off16, off8, offc, nxt, u, kv, p.hkv, k, v, kb2, vb16);
   int buf = 0;
   // Per step: barrier (step n is in LDS, the other buffer is free), write the
   // prefetched step n+1 to the other buffer, issue the loads of step n+2,
@@ -714,9 +716,9 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
       uniform(nn);
     }
     if (nxt.kind != kDone)
-      store_step<D, NW, RT>(pf, DT == kFP8 && nxt.kind == kExact, nxt.kind == kCorr, Ks[buf ^ 1],
+      store_step<D, NW, RT, CORR>(pf, DT == kFP8 && nxt.kind == kExact, nxt.kind == kCorr, Ks[buf ^ 1],
                             Kl[buf ^ 1], Vt[buf ^ 1]);
-    if (nn.kind != kDone) fetch_step<DT, D, NW, RT>(pf, off16, off8, offc, nn, u, kv, p.hkv, k, v, kb2, vb16);
+    if (nn.kind != kDone) fetch_step<DT, D, NW, RT, CORR>(pf, off16, off8, offc, nn, u, kv, p.hkv, k, v, kb2, vb16);
     if (wave_active) {
       int mode, key0 = 0;
       uint64_t todo = 0;
@@ -727,7 +729,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
         mode = kCorrMode;
         todo = chunk_todo(selbits, cur.c, I);
       }
-      compute_step<D, NW, RT>(Ks[buf], Kl[buf], Vt[buf], qf, oacc, m_run, l_run, c, mode, key0, s.len,
+      compute_step<D, NW, RT, CORR>(Ks[buf], Kl[buf], Vt[buf], qf, oacc, m_run, l_run, c, mode, key0, s.len,
                               qpos, todo, bias);
     }
     cur = nxt;
@@ -1007,7 +1009,10 @@ size_t attn_workspace_bytes(const Plan& p, int splits) {
   return bytes;
 }
 
-template <int DT, int D, int NW, int RT>
+// CORR: the instantiation with correction steps.  Launches without them (the
+// dense path, correction off) use one compiled without, whose plain steps keep
+// no registers for the pooled keys' lo rows.
+template <int DT, int D, int NW, int RT, bool CORR>
 static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs& a,
                                 hipStream_t st) {
   const int rows = AttnCfg<D, NW, RT>::ROWS;
@@ -1038,7 +1043,7 @@ static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs&
   const int splits = a.splits;
   const int corr = a.correction && !a.dense;
   if (splits == 1) {
-    hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT, false>), dim3((unsigned)base), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT, false, CORR>), dim3((unsigned)base), dim3(NW * 64), 0,
                        st, pl, kv, a.q, a.k, a.v, (const uint16_t*)kb2, (const uint16_t*)vb16,
                        a.cu, a.idx, c, a.v_scale, corr, a.dense, units_per_seg, 1,
                        (uint16_t*)a.out, a.lse, nullptr, nullptr, nullptr, nullptr);
@@ -1058,10 +1063,10 @@ static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs&
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(&attn_mfma_kernel<DT, D, NW, RT, true>), NW * 64, 0);
+        &per_cu, reinterpret_cast<const void*>(&attn_mfma_kernel<DT, D, NW, RT, true, CORR>), NW * 64, 0);
   if (e != hipSuccess) return e;
   const int64_t grid = std::min<int64_t>(split_items(p, splits), (int64_t)cus * std::max(1, per_cu));
-  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT, true, CORR>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      st, pl, kv, a.q, a.k, a.v, (const uint16_t*)kb2, (const uint16_t*)vb16,
                      a.cu, a.idx, c, a.v_scale, corr, a.dense, units_per_seg, splits,
                      (uint16_t*)a.out, a.lse, part_o, part_ml, items, queue);
@@ -1076,9 +1081,14 @@ template <int DT, int D>
 static hipError_t launch_mfma_d(const Plan& p, const KVDesc& kv, const AttnArgs& a,
                                 hipStream_t st) {
   const int rows = p.g * p.B;
-  if (rows >= 256) return launch_mfma_t<DT, D, 8, 1>(p, kv, a, st);
-  if (rows >= 128) return launch_mfma_t<DT, D, 4, 1>(p, kv, a, st);
-  return launch_mfma_t<DT, D, 2, 1>(p, kv, a, st);
+  if (a.correction && !a.dense) {
+    if (rows >= 256) return launch_mfma_t<DT, D, 8, 1, true>(p, kv, a, st);
+    if (rows >= 128) return launch_mfma_t<DT, D, 4, 1, true>(p, kv, a, st);
+    return launch_mfma_t<DT, D, 2, 1, true>(p, kv, a, st);
+  }
+  if (rows >= 256) return launch_mfma_t<DT, D, 8, 1, false>(p, kv, a, st);
+  if (rows >= 128) return launch_mfma_t<DT, D, 4, 1, false>(p, kv, a, st);
+  return launch_mfma_t<DT, D, 2, 1, false>(p, kv, a, st);
 }
 
 hipError_t launch_attn_mfma(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
