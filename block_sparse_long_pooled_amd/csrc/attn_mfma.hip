@@ -221,13 +221,17 @@ struct AttnCfg {
   static constexpr int KL = (KUN + NT - 1) / NT;
   static constexpr int VL = (VPN + NT - 1) / NT;
   static constexpr int KLD = D + 8;          // padded K row (bf16)
+  // lo rows of a correction step, loaded straight into LDS as [16-byte dim
+  // chunk][key]: NCH chunk rows of KCS bytes, CPW of them per wave
+  static constexpr int NCH = D / 8;
+  static constexpr int KCS = kKeys * 16;
+  static constexpr int CPW = NCH / NW;
   static constexpr int VLD = kKeys + 8;      // padded V^T row (bf16)
 };
 
 template <int D, int NW, int RT>
 struct Prefetch {
   u32x4_t k[AttnCfg<D, NW, RT>::KL];
-  u32x4_t kl[AttnCfg<D, NW, RT>::KL];  // correction steps: the lo rows of K
   u32x4_t v0[AttnCfg<D, NW, RT>::VL];  // key 2a of the pair
   u32x4_t v1[AttnCfg<D, NW, RT>::VL];  // key 2a + 1
 };
@@ -277,8 +281,8 @@ __device__ __forceinline__ const char* uniform_ptr(const void* p) {
 // row, {hi, lo}, Hkv, D] bf16 layout.
 template <int D, int NW, int RT>
 struct CorrOffsets {
-  uint32_t k[AttnCfg<D, NW, RT>::KL];   // hi rows
-  uint32_t kl[AttnCfg<D, NW, RT>::KL];  // lo rows
+  uint32_t k[AttnCfg<D, NW, RT>::KL];    // hi rows
+  uint32_t kl[AttnCfg<D, NW, RT>::CPW];  // lo rows: key = lane, this wave's chunks
 };
 
 template <int D, int NW, int RT>
@@ -292,9 +296,29 @@ __device__ __forceinline__ CorrOffsets<D, NW, RT> corr_offsets(int hkv) {
     const int f = min(tid + i * C::NT, C::KUN - 1);
     const int key = f / C::KU;
     o.k[i] = (uint32_t)(2 * key) * row_bytes + (uint32_t)(f % C::KU) * 16;
-    o.kl[i] = (uint32_t)(2 * key + 1) * row_bytes + (uint32_t)(f % C::KU) * 16;
   }
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int i = 0; i < C::CPW; ++i)
+    o.kl[i] = (uint32_t)(2 * lane + 1) * row_bytes + (uint32_t)(wave + i * NW) * 16;
   return o;
+}
+
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// One wave-wide load of 16 bytes per lane from a raw buffer straight into LDS
+// at lds_addr + 16*lane (gfx950 buffer_load_dwordx4 ... lds).  Inline
+// assembly, so the compiler does not track it: it would otherwise wait for it
+// before every LDS access.  Its data has landed once a later load of the same
+// wave has (loads complete in order): the kernel issues it before the V loads
+// of the same step and stores those V registers before the next barrier.  M0
+// holds the LDS address; one wait state separates its write from the load.
+__device__ __forceinline__ void lds_load16(i32x4_t rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
 }
 
 // Global -> registers for one step.  Exact steps read tokens key0.. of the
@@ -315,7 +339,8 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
                                            const CorrOffsets<D, NW, RT>& offc, const Step& st,
                                            const UnitCtx& u, const KVDesc& kv, int hkv,
                                            const void* k, const void* v,
-                                           const uint16_t* kb2, const uint16_t* vb16) {
+                                           const uint16_t* kb2, const uint16_t* vb16,
+                                           uint16_t* kl_slot) {
   using C = AttnCfg<D, NW, RT>;
   constexpr int PAIRS = kKeys / 2;
   constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
@@ -371,9 +396,16 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
         pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(exact ? off16.k[i] : offc.k[i]),
                                                         0, 0);
       if (CORR && !exact) {
+        // the lo rows go straight to LDS, [chunk][key], between the K and the
+        // V loads of the step
+        const uint64_t a = reinterpret_cast<uint64_t>(ksrc + kb0);
+        const i32x4_t rw = {uni((int)(uint32_t)a), uni((int)(uint32_t)(a >> 32)), uni(nrec_k),
+                            kRsrcWord3};
+        const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t)kl_slot;
+        const int wave = uni(threadIdx.x >> 6);
 #pragma unroll
-        for (int i = 0; i < C::KL; ++i)
-          pf.kl[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)offc.kl[i], 0, 0);
+        for (int i = 0; i < C::CPW; ++i)
+          lds_load16(rw, uni((int)(base + (uint32_t)(wave + i * NW) * C::KCS)), offc.kl[i]);
       }
 #pragma unroll
       for (int i = 0; i < C::VL; ++i) {
@@ -429,8 +461,8 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
 // Registers -> LDS: K row-major, V transposed with permuted key columns; both
 // with padded rows so the 16-byte operand reads of 16 lanes hit distinct banks.
 template <int D, int NW, int RT, bool CORR>
-__device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, bool widen, bool corr,
-                                           uint16_t* Ks, uint16_t* Kl, uint16_t* Vt) {
+__device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, bool widen,
+                                           uint16_t* Ks, uint16_t* Vt) {
   using C = AttnCfg<D, NW, RT>;
   const int tid = threadIdx.x;
 #pragma unroll
@@ -440,7 +472,6 @@ __device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, bool w
     const int key = f / C::KU, un = f % C::KU;
     *reinterpret_cast<u32x4_t*>(Ks + key * C::KLD + un * 8) =
         widen ? e4m3x8_to_bf16x8(pf.k[i][0], pf.k[i][1]) : pf.k[i];
-    if (CORR && corr) *reinterpret_cast<u32x4_t*>(Kl + key * C::KLD + un * 8) = pf.kl[i];
   }
 #pragma unroll
   for (int i = 0; i < C::VL; ++i) {
@@ -501,8 +532,24 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
     }
   };
   // a correction step's pooled logits: the lo rows' products first (the
-  // small terms), then the hi rows', into the same accumulators
-  if (CORR && mode == kCorrMode) qk(Kl);
+  // small terms), then the hi rows', into the same accumulators.  The lo rows
+  // are [16-byte dim chunk][key]: the operand of key kt*32 + key_l, dims
+  // 16 ks + 8 half .. +7, is chunk 2 ks + half.
+  if (CORR && mode == kCorrMode) {
+    const char* lb = reinterpret_cast<const char*>(Kl) + half * C::KCS + key_l * 16;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8_t a =
+            *reinterpret_cast<const bf16x8_t*>(lb + ks * 2 * C::KCS + kt * 512);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          sacc[rt][kt] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rt][ks], sacc[rt][kt], 0, 0, 0);
+      }
+    }
+  }
   qk(Ks);
   // masks: diagonal block (token causality and the request end) or the
   // correction chunk's todo bits; branch-free per element, uniform per step
@@ -601,8 +648,9 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   }
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKeys * C::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VLD];
-  // correction steps: the lo rows of the pooled keys (a stub without them)
-  __shared__ __attribute__((aligned(16))) uint16_t Kl[2][CORR ? kKeys * C::KLD : 8];
+  // correction steps: the lo rows of the pooled keys, a ring of three slots
+  // (the steps being multiplied, staged and loaded); a stub without them
+  __shared__ __attribute__((aligned(16))) uint16_t Kl[3][CORR ? C::NCH * kKeys * 8 : 8];
   __shared__ uint32_t selbits[kMaxBlocksPerSeq / 32];
   __shared__ int next_item;
 
@@ -689,9 +737,9 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   Prefetch<D, NW, RT> pf;
   Step cur = first_step(u, idx, selbits, correction);
   if (cur.kind != kDone) {
-    fetch_step<DT, D, NW, RT, CORR>(pf, off16, off8, offc, cur, u, kv, p.hkv, k, v, kb2, vb16);
-    store_step<D, NW, RT, CORR>(pf, DT == kFP8 && cur.kind == kExact, cur.kind == kCorr, Ks[0], Kl[0],
-                          Vt[0]);
+    fetch_step<DT, D, NW, RT, CORR>(pf, off16, off8, offc, cur, u, kv, p.hkv, k, v, kb2, vb16,
+                                    Kl[0]);
+    store_step<D, NW, RT, CORR>(pf, DT == kFP8 && cur.kind == kExact, Ks[0], Vt[0]);
   }
   uniform(cur);
   // the query rows and the first step have arrived; saying so here keeps the
@@ -700,8 +748,11 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   Step nxt = cur;
   if (cur.kind != kDone) advance(nxt, u, idx, selbits, correction);
   uniform(nxt);
-  if (nxt.kind != kDone) fetch_step<DT, D, NW, RT, CORR>(pf, off16, off8, offc, nxt, u, kv, p.hkv, k, v, kb2, vb16);
+  if (nxt.kind != kDone)
+    fetch_step<DT, D, NW, RT, CORR>(pf, off16, off8, offc, nxt, u, kv, p.hkv, k, v, kb2, vb16,
+                                    Kl[1]);
   int buf = 0;
+  int ls = 0;  // Kl slot of step n (n+1 and n+2 follow, modulo 3)
   // Per step: barrier (step n is in LDS, the other buffer is free), write the
   // prefetched step n+1 to the other buffer, issue the loads of step n+2,
   // multiply step n.  A wave that has written its share starts computing
@@ -716,9 +767,11 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
       uniform(nn);
     }
     if (nxt.kind != kDone)
-      store_step<D, NW, RT, CORR>(pf, DT == kFP8 && nxt.kind == kExact, nxt.kind == kCorr, Ks[buf ^ 1],
-                            Kl[buf ^ 1], Vt[buf ^ 1]);
-    if (nn.kind != kDone) fetch_step<DT, D, NW, RT, CORR>(pf, off16, off8, offc, nn, u, kv, p.hkv, k, v, kb2, vb16);
+      store_step<D, NW, RT, CORR>(pf, DT == kFP8 && nxt.kind == kExact, Ks[buf ^ 1], Vt[buf ^ 1]);
+    // slot ls + 2 held step n-1, which every wave finished before the barrier
+    if (nn.kind != kDone)
+      fetch_step<DT, D, NW, RT, CORR>(pf, off16, off8, offc, nn, u, kv, p.hkv, k, v, kb2, vb16,
+                                      Kl[ls == 0 ? 2 : ls - 1]);
     if (wave_active) {
       int mode, key0 = 0;
       uint64_t todo = 0;
@@ -729,12 +782,13 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
         mode = kCorrMode;
         todo = chunk_todo(selbits, cur.c, I);
       }
-      compute_step<D, NW, RT, CORR>(Ks[buf], Kl[buf], Vt[buf], qf, oacc, m_run, l_run, c, mode, key0, s.len,
+      compute_step<D, NW, RT, CORR>(Ks[buf], Kl[ls], Vt[buf], qf, oacc, m_run, l_run, c, mode, key0, s.len,
                               qpos, todo, bias);
     }
     cur = nxt;
     nxt = nn;
     buf ^= 1;
+    ls = ls == 2 ? 0 : ls + 1;
   }
 
   // ---- epilogue: l over all keys of the row = both lane halves.  A split
