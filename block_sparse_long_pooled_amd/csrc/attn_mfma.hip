@@ -18,9 +18,9 @@
 // the correction chunks of 64 pooled blocks that hold at least one block of
 // todo = valid & ~selected (valid = J <= I-1, fully visible to the tile).
 // A correction step's 64 keys are 64 pooled means as bf16 pairs hi + lo
-// (the float32 mean to within 2^-18 of itself), hi in the K buffer and lo in
-// a second one; both products accumulate into the same scores, so the
-// pooled logits carry no bf16 rounding.
+// (the float32 mean to within 2^-18 of itself), hi in the K buffer and lo
+// loaded straight into a ring of LDS slots; both products accumulate into
+// the same scores, so the pooled logits carry no bf16 rounding.
 // Every thread derives the same sequence, so no step needs a vote.  After
 // the step's barrier each wave writes the prefetched step n+1 into the other
 // LDS buffer, issues the global loads of step n+2 into registers and then
