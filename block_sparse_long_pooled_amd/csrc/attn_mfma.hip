@@ -129,6 +129,7 @@ struct UnitCtx {
   int beg, end;  // the unit's share of the CSR positions of its segment
   int dense;     // blocks are J = t for t in [0, I]: no index list
   int c0, cstep; // correction chunks c0, c0 + cstep, ... belong to the unit
+  int kend;      // keys >= kend are invisible to every row of the unit
 };
 
 // KV splits a segment actually uses, at most `splits`: one per 24 steps of
@@ -162,15 +163,16 @@ __device__ __forceinline__ void find_chunk(Step& st, const uint32_t* selbits, in
 }
 
 // The step after `st`; identical in every thread.  Exact steps run over the
-// selected blocks backwards, B/64 halves each, skipping a second half that
-// lies past the end of a short last block; then come the correction chunks.
+// selected blocks backwards, B/64 halves each, skipping a half that starts
+// past the unit's key limit (the end of a short last block, or keys after
+// the unit's last query position); then come the correction chunks.
 // idx[t-1] is loaded at every exact step and first used one step later, so
 // no step waits for it.
 __device__ __forceinline__ void advance(Step& st, const UnitCtx& u, const int32_t* idx,
                                         const uint32_t* selbits, int correction) {
   if (st.kind == kExact) {
     ++st.hf;
-    if (st.hf == u.B / kKeys || st.J * u.B + st.hf * kKeys >= u.len) {
+    if (st.hf == u.B / kKeys || st.J * u.B + st.hf * kKeys >= u.kend) {
       st.hf = 0;
       --st.t;
       st.J = st.Jn;
@@ -669,9 +671,13 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   // positions, balanced by count, and every ns-th correction chunk
   const int beg0 = dense ? 0 : cu[seg], n_sel = (dense ? I + 1 : cu[seg + 1]) - beg0;
   const int ns = splits == 1 ? 1 : segment_splits(n_sel, I, p.B, correction, splits);
+  // the unit's last query position bounds the keys it can see: a 64-key
+  // half of the diagonal block past it is skipped (all its keys are masked)
+  const int qmax = q0 + max(min(R, (mt + 1) * C::ROWS) - 1, 0) / p.g;
   UnitCtx u{b, h, I, s.len, s.kv_start, s.pool_base, p.B,
             beg0 + (int)((int64_t)sp * n_sel / ns),
-            beg0 + (int)((int64_t)(sp + 1) * n_sel / ns), dense, sp, ns};
+            beg0 + (int)((int64_t)(sp + 1) * n_sel / ns), dense, sp, ns,
+            min(s.len, qmax + 1)};
 
   // ---- this lane's query rows (B operands of Q K^T), one per row tile
   const int row0 = mt * C::ROWS + wave * RT * 32;
