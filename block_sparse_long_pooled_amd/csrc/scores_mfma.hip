@@ -25,10 +25,12 @@
 // as the B operand, so in the 32x32 accumulator every lane owns one key
 // block J (its column) and 16 rows.  Each lane reduces its rows in-lane
 // (max, then sum of exp2), the two lane halves combine with
-// v_permlane32_swap, the waves combine through LDS, and one wave turns the
-// chunk into E_J = S_J * 2^(m_J - M_c) with the chunk maximum M_c (the
-// per-chunk maximum of the V2 index buffer).  A final pass rescales E_J by
-// 2^(M_c - M_I) and divides by the row total.
+// v_permlane32_swap, and the waves' partials (m, S) meet in LDS, where each
+// wave merges 32/NW of the chunk's blocks over the NW partials with
+// shuffles, so no wave does more of it than another.  The per-block maxima
+// m_J stay in LDS and the sums S_J in the score row; at the end every
+// thread takes part in M_I = max_J m_J, the total sum_J S_J 2^(m_J - M_I)
+// (float64) and the scores S_J 2^(m_J - M_I) / total.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -52,6 +54,29 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// x from lane ^ OFF (OFF < 32): ds_swizzle in its xor mode needs no lane-index
+// registers, which a loop that holds the query rows cannot spare.
+template <int OFF>
+__device__ __forceinline__ float swz_xor(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (OFF << 10) | 0x1f));
+}
+
+// max over aligned groups of N lanes (N = 4, 8 or 16), in a fixed order
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 16) x = fmaxf(x, swz_xor<8>(x));
+  if constexpr (N >= 8) x = fmaxf(x, swz_xor<4>(x));
+  x = fmaxf(x, swz_xor<2>(x));
+  return fmaxf(x, swz_xor<1>(x));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 16) x += swz_xor<8>(x);
+  if constexpr (N >= 8) x += swz_xor<4>(x);
+  x += swz_xor<2>(x);
+  return x + swz_xor<1>(x);
+}
+
 // Exact three-term split of a float into bf16 bit patterns (x = hi + mid + lo).
 __device__ __forceinline__ void split3(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
   const uint32_t xb = __float_as_uint(x);
@@ -64,23 +89,25 @@ __device__ __forceinline__ void split3(float x, uint16_t& hi, uint16_t& mid, uin
   lo = (uint16_t)(__float_as_uint(r2) >> 16);
 }
 
-// 8 consecutive query elements as bf16 (exact for bf16 and e4m3 inputs).
+// 8 consecutive query elements as bf16 (exact for bf16 and e4m3 inputs).  An
+// e4m3 value has 4 significant bits, so its float32 bits end in 16 zeros and
+// the upper halves of two v_cvt_pk_f32_fp8 results pack into bf16 pairs.
 template <int DT>
 __device__ __forceinline__ uint4 load_q8_bf16(const typename Elem<DT>::T* p, int64_t off) {
   if constexpr (DT == kBF16) {
     return *reinterpret_cast<const uint4*>(p + off);
   } else {
     const uint2 u = *reinterpret_cast<const uint2*>(p + off);
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t word = i < 2 ? u.x : u.y;
-      const int sh = 16 * (i & 1);
-      const uint32_t a = __float_as_uint(e4m3_to_f32((uint8_t)(word >> sh))) >> 16;
-      const uint32_t b = __float_as_uint(e4m3_to_f32((uint8_t)(word >> (sh + 8)))) >> 16;
-      w[i] = a | (b << 16);
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, false);  // bytes 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, true);   // bytes 2, 3
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, true);
+    constexpr uint32_t hi16 = 0x07060302u;  // upper half of src1, then of src0
+    return make_uint4(
+        __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), hi16),
+        __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), hi16),
+        __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), hi16),
+        __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), hi16));
   }
 }
 
@@ -104,8 +131,9 @@ void scores_mfma_kernel(Plan p,
   __shared__ __attribute__((aligned(16))) uint16_t kb[2][3][kChunk * LD];
   __shared__ float part_m[2][NW][kChunk];
   __shared__ float part_s[2][NW][kChunk];
-  __shared__ float fin[2];
-  extern __shared__ float dyn[];  // cmax[nch], csum[nch]
+  __shared__ float red_m[NW];
+  __shared__ double red_s[NW];
+  extern __shared__ float dyn[];  // m_J[nch * 32]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -121,8 +149,7 @@ void scores_mfma_kernel(Plan p,
   const int R = p.g * tile_nq(s, I, p.B);
   const int nJ = I + 1;
   const int nch = (nJ + kChunk - 1) / kChunk;
-  float* cmax = dyn;
-  float* csum = dyn + nch;
+  float* mJ = dyn;
   float* row_out = scores + score_offset(s, h, I);
   const float* kb_head = kbar + ((int64_t)s.pool_base * p.hkv + h) * D;
   const int64_t kb_stride = (int64_t)p.hkv * D;  // floats between pooled rows
@@ -249,59 +276,58 @@ void scores_mfma_kernel(Plan p,
     }
     if (c + 1 < nch) store(buf ^ 1);
     __syncthreads();
-    if (wave == 0 && half == 0) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) m = fmaxf(m, part_m[buf][w][jj]);
-      const float mu = m == -INFINITY ? 0.f : m;
-      float S = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) S += part_s[buf][w][jj] * __builtin_amdgcn_exp2f(part_m[buf][w][jj] - mu);
-      const int J = c * kChunk + jj;
-      const bool okJ = J < nJ;
-      float Mc = okJ ? m : -INFINITY;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) Mc = fmaxf(Mc, __shfl_xor(Mc, off, 32));
-      const float E = okJ ? S * __builtin_amdgcn_exp2f(m - Mc) : 0.f;
-      float tsum = E;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) tsum += __shfl_xor(tsum, off, 32);
-      if (okJ) row_out[J] = E;
-      if (jj == 0) {
-        cmax[c] = Mc;
-        csum[c] = tsum;
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      // this wave's BPW blocks of the chunk: lane (of each half) takes the
+      // partial of row wave sw for block jl, and groups of NW lanes reduce
+      // (max, then the rescaled sum) in a fixed butterfly order
+      constexpr int BPW = kChunk / NW;
+      const int jl = wave * BPW + jj / NW, sw = jj % NW;
+      const float pmv = part_m[buf][sw][jl], psv = part_s[buf][sw][jl];
+      static_assert(NW == 4 || NW == 8 || NW == 16, "combine groups");
+      const float m = group_max<NW>(pmv);
+      const float S =
+          group_sum<NW>(psv * __builtin_amdgcn_exp2f(pmv - (m == -INFINITY ? 0.f : m)));
+      const int J = c * kChunk + jl;
+      if (half == 0 && sw == 0 && J < nJ) {
+        mJ[J] = m;
+        row_out[J] = S;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
-  if (wave == 0) {
-    // global maximum and total over chunks (fixed order: per-lane strided,
-    // then a butterfly), in float64
-    double M = -INFINITY;
-    for (int c = lane; c < nch; c += 64) M = fmax(M, (double)cmax[c]);
+  // M_I, then the total in float64 (per-thread strided, butterflies, waves in
+  // order), then every score; the barrier makes the S_J stores visible
+  float mloc = -INFINITY;
+  for (int J = tid; J < nJ; J += NT) mloc = fmaxf(mloc, mJ[J]);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmax(M, __shfl_xor(M, off));
-    double tot = 0.0;
-    for (int c = lane; c < nch; c += 64) tot += (double)csum[c] * exp2((double)cmax[c] - M);
+  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+  if (lane == 0) red_m[wave] = mloc;
+  __syncthreads();
+  float Mf = -INFINITY;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
-    if (half == 0) {
-      // each of these lanes rescales only the entries it wrote itself
-      const double inv = 1.0 / tot;
-      for (int c = 0; c < nch; ++c) {
-        const int J = c * kChunk + jj;
-        if (J < nJ)
-          row_out[J] = (float)((double)row_out[J] * exp2((double)cmax[c] - M) * inv);
-      }
-    }
-  }
+  for (int w = 0; w < NW; ++w) Mf = fmaxf(Mf, red_m[w]);
+  const double M = (double)Mf;
+  double tloc = 0.0;
+  for (int J = tid; J < nJ; J += NT) tloc += (double)row_out[J] * exp2((double)mJ[J] - M);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tloc += __shfl_xor(tloc, off);
+  if (lane == 0) red_s[wave] = tloc;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tot += red_s[w];
+  const double inv = 1.0 / tot;
+  for (int J = tid; J < nJ; J += NT)
+    row_out[J] = (float)((double)row_out[J] * exp2((double)mJ[J] - M) * inv);
 }
 
 template <int DT, int D, int RT, int NW>
 static hipError_t launch_scores_t(const Plan& p, const void* q, const float* kbar, float c2,
                                   float* scores, hipStream_t st) {
   const int nch = (p.max_nblk + kChunk - 1) / kChunk;
-  const size_t lds = sizeof(float) * 2 * nch;
+  const size_t lds = sizeof(float) * nch * kChunk;
   hipLaunchKernelGGL((scores_mfma_kernel<DT, D, RT, NW>), dim3((unsigned)p.num_segments),
                      dim3(NW * 64), lds, st, p, (const typename Elem<DT>::T*)q, kbar, c2, scores);
   return hipGetLastError();
