@@ -163,6 +163,19 @@ def test_fp8_128k_sampled():
     assert_parity(w, rep)
 
 
+def test_max_blocks_per_request_sampled():
+    # the largest request the library takes: 16384 blocks of 64 tokens (1M
+    # tokens, 1.3e8 score entries), which sizes the score kernel's per-block
+    # maxima in LDS (64 KB), the attention's selection bitmap and the CSR at
+    # their limits; g = 2 gives 128-row tiles
+    w = Workload("max-blocks-1m-b64", (16384 * 64,), 2, 1, 64, 64, "bf16", attractors=4)
+    inp = make_inputs(w, 0)
+    g = run_gpu(w, inp)
+    rep = compare(w, inp, g, tiles=sample_tiles(w, per_head=2))
+    log(f"[parity] {w.name}: {rep} gpu_ms={g.ms:.1f}")
+    assert_parity(w, rep)
+
+
 def test_paged_varlen_6req_sampled():
     w = PAGED_VARLEN
     inp = make_inputs(w, 0)
