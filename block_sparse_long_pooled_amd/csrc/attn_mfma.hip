@@ -44,6 +44,7 @@
 // the output rescale rare.  Correction terms enter as s*c + log2|B_J| with
 // unselected or invisible columns at -inf.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -509,16 +510,12 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
   using C = AttnCfg<D, NW, RT>;
   const int lane = threadIdx.x & 63;
   const int key_l = lane & 31, half = lane >> 5;
+  // Each path's first MFMA starts from a zero accumulator operand (an inline
+  // constant), so no step spends vector moves clearing the scores.
   f32x16_t sacc[RT][2];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[rt][kt][r] = 0.f;
-    }
-  }
-  auto qk = [&](const uint16_t* Kb) __attribute__((always_inline)) {
+  const f32x16_t zero = {};
+  auto qk = [&](const uint16_t* Kb, auto first) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first)::value;
     const uint16_t* kbase = Kb + key_l * C::KLD + half * 8;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
@@ -528,8 +525,8 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
             *reinterpret_cast<const bf16x8_t*>(kbase + kt * 32 * C::KLD + ks * 16);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-          sacc[rt][kt] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rt][ks], sacc[rt][kt], 0, 0, 0);
+          sacc[rt][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              a, qf[rt][ks], (kFirst && ks == 0) ? zero : sacc[rt][kt], 0, 0, 0);
       }
     }
   };
@@ -547,12 +544,14 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
             *reinterpret_cast<const bf16x8_t*>(lb + ks * 2 * C::KCS + kt * 512);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-          sacc[rt][kt] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rt][ks], sacc[rt][kt], 0, 0, 0);
+          sacc[rt][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              a, qf[rt][ks], ks == 0 ? zero : sacc[rt][kt], 0, 0, 0);
       }
     }
+    qk(Ks, std::false_type{});
+  } else {
+    qk(Ks, std::true_type{});
   }
-  qk(Ks);
   // masks: diagonal block (token causality and the request end) or the
   // correction chunk's todo bits; branch-free per element, uniform per step
   if (mode != kPlain) {
