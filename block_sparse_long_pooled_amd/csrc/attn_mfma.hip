@@ -691,20 +691,29 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     qpos[rt] = q0 + (valid[rt] ? r / p.g : 0);
     hqs[rt] = h * p.g + (valid[rt] ? r % p.g : 0);
     const int64_t qoff = (q_row(s, qpos[rt]) * p.hq + hqs[rt]) * D;
+    if constexpr (DT == kFP8) {
+      // every lane loads (a padding row reads the tile's first row), so the
+      // loads issue back to back instead of one round trip per widening
+      uint2 cw[C::KS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4_t w = {0u, 0u, 0u, 0u};
-      if (valid[rt]) {
-        if constexpr (DT == kFP8) {
-          const uint2 cw = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(q) + qoff +
-                                                           ks * 16 + half * 8);
-          w = e4m3x8_to_bf16x8(cw.x, cw.y);
-        } else {
+      for (int ks = 0; ks < C::KS; ++ks)
+        cw[ks] = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(q) + qoff + ks * 16 +
+                                                 half * 8);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        u32x4_t w = e4m3x8_to_bf16x8(cw[ks].x, cw[ks].y);
+        if (!valid[rt]) w = u32x4_t{0u, 0u, 0u, 0u};
+        qf[rt][ks] = __builtin_bit_cast(bf16x8_t, w);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (valid[rt])
           w = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(q) + qoff + ks * 16 +
                                                 half * 8);
-        }
+        qf[rt][ks] = __builtin_bit_cast(bf16x8_t, w);
       }
-      qf[rt][ks] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
 

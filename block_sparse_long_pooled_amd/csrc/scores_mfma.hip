@@ -89,26 +89,19 @@ __device__ __forceinline__ void split3(float x, uint16_t& hi, uint16_t& mid, uin
   lo = (uint16_t)(__float_as_uint(r2) >> 16);
 }
 
-// 8 consecutive query elements as bf16 (exact for bf16 and e4m3 inputs).  An
-// e4m3 value has 4 significant bits, so its float32 bits end in 16 zeros and
-// the upper halves of two v_cvt_pk_f32_fp8 results pack into bf16 pairs.
-template <int DT>
-__device__ __forceinline__ uint4 load_q8_bf16(const typename Elem<DT>::T* p, int64_t off) {
-  if constexpr (DT == kBF16) {
-    return *reinterpret_cast<const uint4*>(p + off);
-  } else {
-    const uint2 u = *reinterpret_cast<const uint2*>(p + off);
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, false);  // bytes 0, 1
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, true);   // bytes 2, 3
-    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, false);
-    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, true);
-    constexpr uint32_t hi16 = 0x07060302u;  // upper half of src1, then of src0
-    return make_uint4(
-        __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), hi16),
-        __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), hi16),
-        __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), hi16),
-        __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), hi16));
-  }
+// 8 e4m3 codes (two little-endian words) as 8 bf16, exactly.  An e4m3 value
+// has 4 significant bits, so its float32 bits end in 16 zeros and the upper
+// halves of two v_cvt_pk_f32_fp8 results pack into bf16 pairs.
+__device__ __forceinline__ uint4 widen_e4m3x8(uint2 u) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, false);  // bytes 0, 1
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, true);   // bytes 2, 3
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, true);
+  constexpr uint32_t hi16 = 0x07060302u;  // upper half of src1, then of src0
+  return make_uint4(__builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), hi16),
+                    __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), hi16),
+                    __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), hi16),
+                    __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), hi16));
 }
 
 }  // namespace
@@ -165,11 +158,26 @@ void scores_mfma_kernel(Plan p,
     const int pos = q0 + (ok ? r / p.g : 0);
     const int hq = h * p.g + (ok ? r % p.g : 0);
     const int64_t qoff = (q_row(s, pos) * p.hq + hq) * D;
+    if constexpr (DT == kFP8) {
+      // every lane loads (a padding row reads the tile's first row), so the
+      // loads issue back to back instead of one round trip per widening
+      uint2 cw[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (ok) u = load_q8_bf16<DT>(q, qoff + ks * 16 + half * 8);
-      qa[t][ks] = __builtin_bit_cast(sbf16x8_t, u);
+      for (int ks = 0; ks < KS; ++ks)
+        cw[ks] = *reinterpret_cast<const uint2*>(q + qoff + ks * 16 + half * 8);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 u = widen_e4m3x8(cw[ks]);
+        if (!ok) u = make_uint4(0, 0, 0, 0);
+        qa[t][ks] = __builtin_bit_cast(sbf16x8_t, u);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (ok) u = *reinterpret_cast<const uint4*>(q + qoff + ks * 16 + half * 8);
+        qa[t][ks] = __builtin_bit_cast(sbf16x8_t, u);
+      }
     }
   }
 
