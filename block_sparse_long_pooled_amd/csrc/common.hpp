@@ -159,12 +159,15 @@ __device__ __forceinline__ void load8(const typename Elem<DT>::T* p, int64_t off
       out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   } else {
+    // OCP e4m3 codes widened by v_cvt_pk_f32_fp8 (two codes per instruction,
+    // exact: every e4m3 value is a float32)
     const uint2 u = *reinterpret_cast<const uint2*>(p + off);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[i] = e4m3_to_f32((uint8_t)(u.x >> (8 * i)));
-      out[4 + i] = e4m3_to_f32((uint8_t)(u.y >> (8 * i)));
-    }
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, true);
+    out[0] = a[0]; out[1] = a[1]; out[2] = b[0]; out[3] = b[1];
+    out[4] = c[0]; out[5] = c[1]; out[6] = d[0]; out[7] = d[1];
   }
 }
 
