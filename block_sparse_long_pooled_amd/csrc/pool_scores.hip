@@ -45,7 +45,35 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Plan p, KVDesc kv,
   const typename Elem<DT>::T* x = is_v ? v : k;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (active) {
-    for (int r = rg; r < cnt; r += rg_n) {
+    // four rows' loads in flight at a time, added in row order as one by one
+    int r = rg;
+    for (; r + 3 * rg_n < cnt; r += 4 * rg_n) {
+      // all four rows first (their page-table entries in one batch of loads),
+      // then the data
+      int64_t rows[4];
+      if (kv.page_table != nullptr) {
+        int32_t phys[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          phys[u] = kv.page_table[(int64_t)b * kv.max_pages + ((j0 + r + u * rg_n) >> kv.page_shift)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          rows[u] = ((int64_t)phys[u] << kv.page_shift) |
+                    (int64_t)((j0 + r + u * rg_n) & ((1 << kv.page_shift) - 1));
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rows[u] = (int64_t)s.kv_start + j0 + r + u * rg_n;
+      }
+      float e[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load8<DT>(x, (rows[u] * p.hkv + h0) * D + col8 * 8, e[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += e[u][i];
+      }
+    }
+    for (; r < cnt; r += rg_n) {
       const int64_t row = kv.row(b, s.kv_start, j0 + r);
       float e[8];
       load8<DT>(x, (row * p.hkv + h0) * D + col8 * 8, e);
