@@ -220,9 +220,29 @@ void scores_mfma_kernel(Plan p,
   store(0);
   __syncthreads();
 
+  // merge of chunk cc's row partials: wave w takes blocks w*BPW .. +BPW-1 of
+  // the chunk, a lane (of each half) the partial of row wave sw for block jl,
+  // and groups of NW lanes reduce (max, then the rescaled sum) in a fixed
+  // butterfly order.  The partials are double buffered, so the merge of
+  // chunk c-1 runs during chunk c, beside its matrix work.
+  auto combine = [&](int cc) __attribute__((always_inline)) {
+    constexpr int BPW = kChunk / NW;
+    static_assert(NW == 4 || NW == 8 || NW == 16, "combine groups");
+    const int jl = wave * BPW + jj / NW, sw = jj % NW;
+    const float pmv = part_m[cc & 1][sw][jl], psv = part_s[cc & 1][sw][jl];
+    const float m = group_max<NW>(pmv);
+    const float S = group_sum<NW>(psv * __builtin_amdgcn_exp2f(pmv - (m == -INFINITY ? 0.f : m)));
+    const int J = cc * kChunk + jl;
+    if (half == 0 && sw == 0 && J < nJ) {
+      mJ[J] = m;
+      row_out[J] = S;
+    }
+  };
+
   for (int c = 0; c < nch; ++c) {
     const int buf = c & 1;
     if (c + 1 < nch) fetch(c + 1);
+    if (c > 0) combine(c - 1);
     float pm = -INFINITY, ps = 0.f;
     if (wave_active) {
       sf32x16_t acc[RT];
@@ -284,26 +304,8 @@ void scores_mfma_kernel(Plan p,
     }
     if (c + 1 < nch) store(buf ^ 1);
     __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      // this wave's BPW blocks of the chunk: lane (of each half) takes the
-      // partial of row wave sw for block jl, and groups of NW lanes reduce
-      // (max, then the rescaled sum) in a fixed butterfly order
-      constexpr int BPW = kChunk / NW;
-      const int jl = wave * BPW + jj / NW, sw = jj % NW;
-      const float pmv = part_m[buf][sw][jl], psv = part_s[buf][sw][jl];
-      static_assert(NW == 4 || NW == 8 || NW == 16, "combine groups");
-      const float m = group_max<NW>(pmv);
-      const float S =
-          group_sum<NW>(psv * __builtin_amdgcn_exp2f(pmv - (m == -INFINITY ? 0.f : m)));
-      const int J = c * kChunk + jl;
-      if (half == 0 && sw == 0 && J < nJ) {
-        mJ[J] = m;
-        row_out[J] = S;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
   }
+  combine(nch - 1);
   __syncthreads();
   // M_I, then the total in float64 (per-thread strided, butterflies, waves in
   // order), then every score; the barrier makes the S_J stores visible
