@@ -163,6 +163,16 @@ def test_fp8_128k_sampled():
     assert_parity(w, rep)
 
 
+@pytest.mark.parametrize("w", [SWEEP_BF16_64K, FP8_128K], ids=lambda w: w.name)
+def test_full_size_second_seed_sampled(w):
+    # the full-size workloads on fresh inputs (seed 1), as the bench runs them
+    inp = make_inputs(w, 1)
+    g = run_gpu(w, inp)
+    rep = compare(w, inp, g, tiles=sample_tiles(w, per_head=2, seed=1))
+    log(f"[parity] {w.name} seed 1: {rep} gpu_ms={g.ms:.1f}")
+    assert_parity(w, rep)
+
+
 def test_max_blocks_per_request_sampled():
     # the largest request the library takes: 16384 blocks of 64 tokens (1M
     # tokens, 1.3e8 score entries), which sizes the score kernel's per-block
