@@ -884,8 +884,9 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
 
 // Merge of the KV splits of the rows of every split segment: with M =
 // max_u m_u and weights w_u = l_u 2^(m_u - M), O = sum_u w_u O_u / sum_u w_u
-// and LSE = M ln 2 + ln sum_u w_u (the split-combine of "FlashPrefill V2",
-// Sec. 3.3 KV splitting).  One workgroup per segment (b, h, I); segments that
+// and LSE = M ln 2 + ln sum_u w_u (the KV splits of "FlashPrefill V2", CSR
+// paragraph, Eq. 18; the combine is the online-softmax merge of the PRR review
+// page, Sec. 4.3 Eq. 6).  One workgroup per segment (b, h, I); segments that
 // were not split wrote their rows directly and are skipped.
 template <int D>
 __global__ __launch_bounds__(256) void merge_splits_kernel(Plan p, const int32_t* __restrict__ cu,
@@ -931,8 +932,9 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(Plan p, const int32_t
   }
 }
 
-// Work list of a split launch ("FlashPrefill V2", Sec. 3.3: splits balanced by
-// selected count, heaviest work first): one workgroup walks the segments in
+// Work list of a split launch ("FlashPrefill V2", CSR paragraph, Eq. 18, and
+// the scheduling paragraph after it: splits balanced by selected count,
+// heaviest work first): one workgroup walks the segments in
 // the order of the unsplit launch (longest request first, tiles in
 // descending I, KV head innermost), gives each its split count from its
 // selected count and writes one item (segment << 8 | row block << 4 | split)

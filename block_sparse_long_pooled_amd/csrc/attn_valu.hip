@@ -1,8 +1,9 @@
 // Stage 3, vector-ALU form: block-sparse causal online-softmax attention
 // with mean correction, one query row per lane ("FlashPrefill V2", Sec. 3.1
 // last sentence, Sec. 3.2 / Fig. 3 correction path, PackGQA and CSR
-// paragraphs).  This form serves float32 inputs (exact fp32 arithmetic, no
-// matrix cores) and small problems of every dtype.
+// paragraphs).  This form serves float32 inputs only (exact fp32
+// arithmetic, no matrix cores); bf16 and fp8 inputs always take the
+// matrix-core kernels.
 //
 // Work unit: (segment (b, h, I), 64 consecutive PackGQA rows of tile I).
 // Packed row r of the tile is position I*B + r / g of query head h*g + r % g.
@@ -200,14 +201,9 @@ static hipError_t launch_attn_valu_t(const Plan& p, const KVDesc& kv, const Attn
 
 hipError_t launch_attn_valu(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
                             hipStream_t st) {
-  if (p.d == 128) {
-    if (dtype == kF32) return launch_attn_valu_t<kF32, 128>(p, kv, a, st);
-    if (dtype == kBF16) return launch_attn_valu_t<kBF16, 128>(p, kv, a, st);
-    return launch_attn_valu_t<kFP8, 128>(p, kv, a, st);
-  }
-  if (dtype == kF32) return launch_attn_valu_t<kF32, 64>(p, kv, a, st);
-  if (dtype == kBF16) return launch_attn_valu_t<kBF16, 64>(p, kv, a, st);
-  return launch_attn_valu_t<kFP8, 64>(p, kv, a, st);
+  if (dtype != kF32) return hipErrorInvalidValue;  // bf16 / fp8 run on the matrix cores
+  return p.d == 128 ? launch_attn_valu_t<kF32, 128>(p, kv, a, st)
+                    : launch_attn_valu_t<kF32, 64>(p, kv, a, st);
 }
 
 }  // namespace bslp

@@ -96,7 +96,8 @@ typedef struct bslp_problem {
   const int32_t* page_table; /* DEVICE [num_seqs, max_pages_per_seq] or NULL */
   int32_t page_size;
   int32_t max_pages_per_seq;
-  /* KV splitting of the attention ("FlashPrefill V2", Sec. 3.3: a work unit's
+  /* KV splitting of the attention ("FlashPrefill V2", CSR paragraph, Eq. 18,
+   * and the scheduling paragraph after it: a work unit's
    * selected blocks are cut into contiguous shares balanced by count, each
    * run by its own workgroup, and the partial results are merged through
    * their log-sum-exp).  0 = automatic (split only when the launch has fewer
@@ -152,7 +153,12 @@ bslp_status bslp_get_sizes(const bslp_problem* problem, bslp_sizes* out);
  *   tile's g*|tile| rows r (block-causal, no token mask in the diagonal
  *   block), M_I = max_{r, J<=I} s_rJ, S'_IJ = sum_r exp(s_rJ - M_I),
  *   Score_IJ = S'_IJ / sum_{K<=I} S'_IK, written to scores (float32 rows as
- *   described above).  Logits are accumulated in float64.
+ *   described above).  Accuracy: float32 inputs accumulate the logits in
+ *   float64 on the vector ALUs.  bf16 / fp8 inputs run on the matrix cores:
+ *   q is exact in bf16 and kbar is split exactly into three bf16 terms, so
+ *   every product is exact and only the float32 accumulation rounds; the
+ *   scores carry a relative error of order 1e-5 (measured below 1e-5 on the
+ *   64K and 128K workloads).
  *
  * q: [T, Hq, d] in the problem dtype.  k, v: [T, Hkv, d], or physical rows
  * [*, Hkv, d] through the page table.  All device pointers. */
@@ -211,9 +217,8 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
 bslp_status bslp_dense_prefill_attn(const bslp_problem* problem, const void* q, const void* k,
                                     const void* v, void* out, float* lse, void* stream);
 
-/* Online per-tensor fp8 quantisation ("FlashPrefill V2", Sec. 3.3 FP8
- * paragraph: e4m3 operands, one absmax-derived scale per tensor, computed on
- * the device): with amax = max_i |x_i|, *scale = amax / 448 (1 if amax is 0)
+/* Online per-tensor fp8 quantisation ("FlashPrefill V2", the FP8 paragraph:
+ * e4m3 operands, one absmax-derived scale per tensor, computed on the device): with amax = max_i |x_i|, *scale = amax / 448 (1 if amax is 0)
  * and codes[i] = e4m3fn(x_i / *scale), rounded to nearest even, saturated at
  * +-448, sign kept (float32 division, correctly rounded).
  *

@@ -7,7 +7,7 @@ Format: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent
 field 0 encodes subnormals m/8 * 2^-6; there are no infinities and the codes
 S.1111.111 are NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
 FlashPrefill V2 feeds Q, K and V as e4m3 with one fp32 scale per tensor
-(FlashPrefill V2, Sec. 3.3 FP8 paragraph); the oracle reads each input as
+(FlashPrefill V2, the FP8 paragraph); the oracle reads each input as
 decode(code) * scale in float64.
 """
 import numpy as np
@@ -46,7 +46,7 @@ def encode_e4m3fn(x) -> np.ndarray:
 
 def quantize_per_tensor(x) -> tuple:
     """Online per-tensor quantisation of Q, K or V to e4m3 (FlashPrefill V2,
-    Sec. 3.3 FP8 paragraph: one absmax-derived scale per tensor): with amax =
+    the FP8 paragraph: one absmax-derived scale per tensor): with amax =
     max |x|, scale = amax / 448 (1 when amax is 0) and code = e4m3(x / scale).
     The scale and the quotient are rounded to float32, the precision the
     device takes these decisions in, so the codes are comparable bit for bit.

@@ -7,9 +7,9 @@ import numpy as np
 import pytest
 
 from harness import (assert_parity, compare, log, make_inputs, run_gpu, sample_tiles,
-                     to_device)
-from workloads import (FP8_128K, GQA_BF16_16K, PAGED_VARLEN, SWEEP_ALPHAS, SWEEP_BF16_64K,
-                       TINY_F32, Workload)
+                     segments, to_device)
+from workloads import (CHUNK_BF16_64K, FP8_128K, GQA_BF16_16K, PAGED_VARLEN, SWEEP_ALPHAS,
+                       SWEEP_BF16_64K, TINY_F32, Workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +65,20 @@ SMALL = [
     # of 64 pooled blocks, the last with a single block
     Workload("corr-chunks-129-blocks", (8200,), 4, 1, 64, 64, "bf16", attractors=4),
     Workload("corr-chunks-fp8", (8200,), 8, 1, 64, 64, "fp8", sigma_c=1.5),
+    # group size 16: 2048-row tiles at B = 128 (block scores beyond the
+    # matrix-core kernel's 1024 rows), 1024-row tiles at B = 64 (16 waves)
+    Workload("g16-b128-bf16", (1000,), 32, 2, 128, 128, "bf16", attractors=4),
+    Workload("g16-b128-fp8", (700,), 16, 1, 64, 128, "fp8", sigma_c=1.5),
+    Workload("g16-b64-bf16", (900,), 16, 1, 128, 64, "bf16", attractors=4),
+    Workload("g16-b64-fp8", (777,), 32, 2, 128, 64, "fp8", sigma_c=1.5),
+    # group sizes that are not powers of two: packed-row divmod, partial
+    # row blocks and row tiles
+    Workload("g3-hq12-hkv4-bf16", (1100,), 12, 4, 128, 128, "bf16", attractors=4),
+    Workload("g3-hq12-hkv4-fp8", (650,), 12, 4, 128, 64, "fp8", sigma_c=1.5),
+    Workload("g5-hq10-hkv2-bf16", (900,), 10, 2, 64, 64, "bf16"),
+    Workload("g6-hq12-hkv2-bf16", (1300,), 12, 2, 128, 128, "bf16", attractors=4, vertical=3),
+    Workload("g12-hq24-hkv2-fp8", (500,), 24, 2, 128, 128, "fp8", sigma_c=1.5),
+    Workload("g7-hq7-hkv1-f32", (300,), 7, 1, 64, 64, "f32"),
 ]
 
 
@@ -139,38 +153,90 @@ def test_deterministic_bitwise():
         assert np.array_equal(getattr(a, name), getattr(b, name), equal_nan=True), name
 
 
-# ----------------------------------------------------------------- full-size configs, sampled
+# ----------------------------------------------------------------- full-size configs
+#
+# Every call passes the whole-array checks (run_gpu).  Every segment's
+# scores and selection are compared with the oracle; attention outputs on
+# every tile of one whole KV head plus sampled tiles of the others.
 
-def test_sweep_64k_sampled():
+WORKERS = 16  # host threads for the oracle (the GPU machine's CPU share)
+
+
+def _dense_error(w, inp, g, tiles):
+    """Max-abs of the GPU's sparse output against exact dense causal attention
+    (the oracle with every block selected), on the given tiles: the error the
+    approximation itself makes, reported, not gated."""
+    import oracle
+    from harness import RequestView
+    err = 0.0
+    views = {}
+    for (b, h, I) in sorted(tiles):
+        if b not in views:
+            views = {b: RequestView(w, inp, b)}
+        rv = views[b]
+        k_h, v_h, kbar_h, vbar_h = rv.head(h)
+        pos, heads, rows = oracle.tile_query_rows(rv.q, h, w.g, w.block, I, rv.q_off)
+        O, _ = oracle.attend_rows(pos, rows, k_h, v_h, kbar_h, vbar_h, list(range(I + 1)), [],
+                                  w.block, w.scale)
+        go = g.out[rv.qstart + pos - rv.q_off, heads]
+        err = max(err, float(np.abs(go - O).max()))
+    return err
+
+
+def _full_size(w, seed, rows=None, whole_head=None, per_head=3, dev=None, inp=None, **kw):
+    from harness import compare_selection, oracle_score_rows
+    inp = inp if inp is not None else make_inputs(w, seed)
+    log(f"[parity] {w.name} seed={seed} {kw}: GPU run")
+    g = run_gpu(w, inp, dev_tensors=dev, **kw)  # whole-array checks inside
+    rows = rows if rows is not None else oracle_score_rows(w, inp, workers=WORKERS)
+    sel = compare_selection(w, g, rows, alpha=kw.get("alpha"))
+    log(f"[parity] {w.name} every segment: {sel}")
+    assert sel.tiles == len(segments(w.seqlens, w.hkv, w.block, w.query_lens))
+    assert sel.sel_mismatch == 0, str(sel)
+    assert sel.score_rel < 1e-4, str(sel)
+    tiles = sample_tiles(w, per_head=per_head, seed=seed)
+    if whole_head is not None:
+        for b, (L, Lq) in enumerate(zip(w.seqlens, w.query_lens)):
+            N = -(-L // w.block)
+            i0 = (L - Lq) // w.block if Lq else N
+            tiles |= {(b, whole_head, I) for I in range(i0, N)}
+    rep = compare(w, inp, g, tiles=tiles, workers=WORKERS, **kw)
+    log(f"[parity] {w.name} attention tiles (KV head {whole_head} whole): {rep} gpu_ms={g.ms:.1f}")
+    assert_parity(w, rep)
+    return inp, g, rows, sel, rep
+
+
+@pytest.mark.timeout(1200)
+def test_sweep_64k_every_segment():
+    # five alphas x correction on/off; scores do not depend on alpha, so the
+    # oracle rows are computed once.  Per alpha: density, output error against
+    # the oracle and against exact dense attention (correction on vs off).
     w = SWEEP_BF16_64K
     inp = make_inputs(w, 0)
     dev = to_device(inp)
-    tiles = sample_tiles(w, per_head=3)
+    from harness import oracle_score_rows
+    rows = oracle_score_rows(w, inp, workers=WORKERS)
+    dense_tiles = sample_tiles(w, per_head=2, heads=[1])
     for a in SWEEP_ALPHAS:
         for corr in (True, False):
-            g = run_gpu(w, inp, alpha=a, correction=corr, dev_tensors=dev)
-            rep = compare(w, inp, g, tiles=tiles, alpha=a, correction=corr)
-            log(f"[parity] {w.name} alpha={a} corr={corr}: {rep} gpu_ms={g.ms:.1f}")
-            assert_parity(w, rep)
+            whole = 3 if (a == 0.05 and corr) else None
+            _, g, _, sel, rep = _full_size(w, 0, rows=rows, whole_head=whole, per_head=2, dev=dev,
+                                           inp=inp, alpha=a, correction=corr)
+            derr = _dense_error(w, inp, g, dense_tiles)
+            log(f"[sweep] alpha={a} correction={corr} density={sel.selected / sel.blocks:.4f} "
+                f"out_err_vs_oracle={rep.out_err:.3e} out_err_vs_dense={derr:.3e}")
 
 
-def test_fp8_128k_sampled():
-    w = FP8_128K
-    inp = make_inputs(w, 0)
-    g = run_gpu(w, inp)
-    rep = compare(w, inp, g, tiles=sample_tiles(w, per_head=3))
-    log(f"[parity] {w.name}: {rep} gpu_ms={g.ms:.1f}")
-    assert_parity(w, rep)
+@pytest.mark.timeout(1200)
+def test_fp8_128k_every_segment():
+    _full_size(FP8_128K, 0, whole_head=2)
 
 
+@pytest.mark.timeout(1200)
 @pytest.mark.parametrize("w", [SWEEP_BF16_64K, FP8_128K], ids=lambda w: w.name)
-def test_full_size_second_seed_sampled(w):
+def test_full_size_second_seed(w):
     # the full-size workloads on fresh inputs (seed 1), as the bench runs them
-    inp = make_inputs(w, 1)
-    g = run_gpu(w, inp)
-    rep = compare(w, inp, g, tiles=sample_tiles(w, per_head=2, seed=1))
-    log(f"[parity] {w.name} seed 1: {rep} gpu_ms={g.ms:.1f}")
-    assert_parity(w, rep)
+    _full_size(w, 1, per_head=2)
 
 
 def test_max_blocks_per_request_sampled():
@@ -186,10 +252,12 @@ def test_max_blocks_per_request_sampled():
     assert_parity(w, rep)
 
 
-def test_paged_varlen_6req_sampled():
-    w = PAGED_VARLEN
-    inp = make_inputs(w, 0)
-    g = run_gpu(w, inp)
-    rep = compare(w, inp, g, tiles=sample_tiles(w, per_head=2))
-    log(f"[parity] {w.name}: {rep} gpu_ms={g.ms:.1f}")
-    assert_parity(w, rep)
+@pytest.mark.timeout(1500)
+def test_paged_varlen_6req_every_segment():
+    _full_size(PAGED_VARLEN, 0, whole_head=5, per_head=2)
+
+
+@pytest.mark.timeout(900)
+def test_chunk_last_8k_of_64k_every_segment():
+    # the chunked-prefill workload the bench times: 8K queries over 64K keys
+    _full_size(CHUNK_BF16_64K, 0, whole_head=6, per_head=2)
