@@ -77,8 +77,10 @@ class Sizes(ctypes.Structure):
 
 
 EXPORTS = ("bslp_get_sizes", "bslp_block_scores", "bslp_select_blocks",
-           "bslp_sparse_prefill_attn", "bslp_dense_prefill_attn", "bslp_quantize_e4m3",
-           "bslp_status_string", "bslp_last_error")
+           "bslp_sparse_prefill_attn", "bslp_sparse_prefill_attn_noalloc",
+           "bslp_dense_prefill_attn", "bslp_quantize_e4m3", "bslp_status_string",
+           "bslp_last_error")
+NOALLOC_SCRATCH_BYTES = 32 << 20  # BSLP_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -99,10 +101,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bslp_select_blocks.argtypes = [P(Problem), P(SelectParams), vp, vp, vp, vp, vp]
     lib.bslp_sparse_prefill_attn.argtypes = [P(Problem), P(SelectParams), vp, vp, vp, vp, vp,
                                              vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.bslp_sparse_prefill_attn_noalloc.argtypes = [P(Problem), P(SelectParams), vp, vp, vp,
+                                                     vp, vp, vp, vp, vp, vp, vp]
     lib.bslp_dense_prefill_attn.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp]
     lib.bslp_quantize_e4m3.argtypes = [ctypes.c_int32, vp, ctypes.c_int64, vp, vp, vp]
     for name in ("bslp_get_sizes", "bslp_block_scores", "bslp_select_blocks",
-                 "bslp_sparse_prefill_attn", "bslp_dense_prefill_attn", "bslp_quantize_e4m3"):
+                 "bslp_sparse_prefill_attn", "bslp_sparse_prefill_attn_noalloc",
+                 "bslp_dense_prefill_attn", "bslp_quantize_e4m3"):
         getattr(lib, name).restype = ctypes.c_int
     lib.bslp_status_string.argtypes = [ctypes.c_int]
     lib.bslp_status_string.restype = ctypes.c_char_p
@@ -202,6 +207,15 @@ def sparse_prefill_attn(problem, params, q, k, v, kbar, vbar, cu, idx, out, lse=
                                                    _stream(stream)))
 
 
+def sparse_prefill_attn_noalloc(problem, params, q, k, v, kbar, vbar, cu, idx, out, lse=None,
+                                stream=None):
+    """sparse_prefill_attn without a workspace: the library's own device
+    scratch array (NOALLOC_SCRATCH_BYTES per GPU) takes its place."""
+    _check(load_library().bslp_sparse_prefill_attn_noalloc(
+        ctypes.byref(problem), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(kbar),
+        _ptr(vbar), _ptr(cu), _ptr(idx), _ptr(out), _ptr(lse), _stream(stream)))
+
+
 def quantize_e4m3(x, codes, scale, stream=None):
     """Online per-tensor e4m3 quantisation of the bf16 or float32 device
     tensor x into the uint8 tensor codes; scale (a one-element device float32
@@ -253,4 +267,4 @@ def prefill(problem, params, q, k, v, bufs: Buffers | None = None, stream=None) 
 __all__ = ["BF16", "F32", "FP8_E4M3", "BslpError", "Buffers", "EXPORTS", "LIB_PATH", "Problem",
            "SelectParams", "Sizes", "block_scores", "dense_prefill_attn", "get_sizes",
            "load_library", "make_params",
-           "make_problem", "prefill", "quantize_e4m3", "select_blocks", "sparse_prefill_attn"]
+           "make_problem", "prefill", "quantize_e4m3", "select_blocks", "sparse_prefill_attn", "sparse_prefill_attn_noalloc"]

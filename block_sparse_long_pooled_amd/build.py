@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbslp.so")
 
-SOURCES = ["api.cpp", "pool_scores.hip", "select.hip", "attn_valu.hip", "attn_mfma.hip", "scores_mfma.hip", "quant.hip"]
+SOURCES = ["api.cpp", "pool_scores.hip", "select.hip", "attn_valu.hip", "attn_mfma.hip", "scores_mfma.hip", "quant.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -151,6 +151,66 @@ bslp_status hip_result(hipError_t e, const char* what) {
   return fail(BSLP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+static_assert(BSLP_NOALLOC_SCRATCH_BYTES == bslp::kNoAllocScratchBytes,
+              "the header states the device scratch size of the no-allocation entry point");
+
+// Stage 3 with a caller workspace, or (noalloc) with the library's device
+// scratch array in its place.
+bslp_status sparse_attn(const bslp_problem* problem, const bslp_select_params* params,
+                        const void* q, const void* k, const void* v, const float* kbar,
+                        const float* vbar, const int32_t* cu, const int32_t* idx, void* out,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                        bool noalloc) {
+  const char* what = noalloc ? "bslp_sparse_prefill_attn_noalloc" : "bslp_sparse_prefill_attn";
+  bslp::Plan plan;
+  bslp::KVDesc kv;
+  bslp::SelectArgs sa;
+  bslp_status st = build_plan(problem, &plan, &kv);
+  if (st != BSLP_OK) return st;
+  st = check_params(params, &sa);
+  if (st != BSLP_OK) return st;
+  if (plan.total_tokens == 0) return BSLP_OK;
+  if (!q || !k || !v || !kbar || !vbar || !cu || !idx || !out)
+    return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  int splits = bslp::attn_splits(plan, problem->dtype, problem->kv_splits);
+  size_t need = bslp::attn_workspace_bytes(plan, splits);
+  if (noalloc) {
+    // an automatic split count falls back to no split when its partial
+    // results do not fit the scratch array; a requested count does not
+    if (need > bslp::kNoAllocScratchBytes && problem->kv_splits == 0 && splits > 1) {
+      splits = 1;
+      need = bslp::attn_workspace_bytes(plan, splits);
+    }
+    if (need > bslp::kNoAllocScratchBytes)
+      return fail(BSLP_ERR_UNSUPPORTED,
+                  std::string(what) + " needs " + std::to_string(need) +
+                      " bytes of scratch, above its fixed " +
+                      std::to_string(bslp::kNoAllocScratchBytes) +
+                      " (pass kv_splits = 1, or use bslp_sparse_prefill_attn with a workspace)");
+    const hipError_t e = bslp::noalloc_scratch(&workspace);
+    if (e != hipSuccess) return hip_result(e, what);
+  } else {
+    if (workspace_bytes < need)
+      return fail(BSLP_ERR_INVALID_ARG, "workspace_bytes " + std::to_string(workspace_bytes) +
+                                            " is below the " + std::to_string(need) +
+                                            " bytes bslp_get_sizes reports");
+    if (need > 0 && !workspace) return fail(BSLP_ERR_INVALID_ARG, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 16)
+      return fail(BSLP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  bslp::AttnArgs a{q, k, v, kbar, vbar, cu, idx, out, lse, workspace,
+                   problem->softmax_scale * host_scale(problem, 0), host_scale(problem, 1),
+                   host_scale(problem, 2), sa.correction, 0, splits};
+  // bf16 and fp8 run on the matrix cores; float32 keeps exact fp32
+  // arithmetic on the vector ALUs.
+  const hipError_t e = problem->dtype == BSLP_F32
+                           ? bslp::launch_attn_valu(plan, kv, problem->dtype, a,
+                                                    (hipStream_t)stream)
+                           : bslp::launch_attn_mfma(plan, kv, problem->dtype, a,
+                                                    (hipStream_t)stream);
+  return hip_result(e, what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -211,36 +271,18 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
                                      const float* vbar, const int32_t* cu, const int32_t* idx,
                                      void* out, float* lse, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-  bslp::Plan plan;
-  bslp::KVDesc kv;
-  bslp::SelectArgs sa;
-  bslp_status st = build_plan(problem, &plan, &kv);
-  if (st != BSLP_OK) return st;
-  st = check_params(params, &sa);
-  if (st != BSLP_OK) return st;
-  if (plan.total_tokens == 0) return BSLP_OK;
-  if (!q || !k || !v || !kbar || !vbar || !cu || !idx || !out)
-    return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
-  const int splits = bslp::attn_splits(plan, problem->dtype, problem->kv_splits);
-  const size_t need = bslp::attn_workspace_bytes(plan, splits);
-  if (workspace_bytes < need)
-    return fail(BSLP_ERR_INVALID_ARG, "workspace_bytes " + std::to_string(workspace_bytes) +
-                                          " is below the " + std::to_string(need) +
-                                          " bytes bslp_get_sizes reports");
-  if (need > 0 && !workspace) return fail(BSLP_ERR_INVALID_ARG, "workspace is NULL");
-  if (reinterpret_cast<uintptr_t>(workspace) % 16)
-    return fail(BSLP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  bslp::AttnArgs a{q, k, v, kbar, vbar, cu, idx, out, lse, workspace,
-                   problem->softmax_scale * host_scale(problem, 0), host_scale(problem, 1),
-                   host_scale(problem, 2), sa.correction, 0, splits};
-  // bf16 and fp8 run on the matrix cores; float32 keeps exact fp32
-  // arithmetic on the vector ALUs.
-  const hipError_t e = problem->dtype == BSLP_F32
-                           ? bslp::launch_attn_valu(plan, kv, problem->dtype, a,
-                                                    (hipStream_t)stream)
-                           : bslp::launch_attn_mfma(plan, kv, problem->dtype, a,
-                                                    (hipStream_t)stream);
-  return hip_result(e, "bslp_sparse_prefill_attn");
+  return sparse_attn(problem, params, q, k, v, kbar, vbar, cu, idx, out, lse, workspace,
+                     workspace_bytes, stream, false);
+}
+
+bslp_status bslp_sparse_prefill_attn_noalloc(const bslp_problem* problem,
+                                             const bslp_select_params* params, const void* q,
+                                             const void* k, const void* v, const float* kbar,
+                                             const float* vbar, const int32_t* cu,
+                                             const int32_t* idx, void* out, float* lse,
+                                             void* stream) {
+  return sparse_attn(problem, params, q, k, v, kbar, vbar, cu, idx, out, lse, nullptr, 0, stream,
+                     true);
 }
 
 bslp_status bslp_dense_prefill_attn(const bslp_problem* problem, const void* q, const void* k,

@@ -55,6 +55,12 @@ size_t attn_workspace_bytes(const Plan& p, int splits);
 hipError_t launch_quantize_e4m3(int src_dtype, const void* x, int64_t n, uint8_t* codes,
                                 float* scale, hipStream_t st);
 
+// Size of the device array that serves as the attention workspace of the
+// entry point that allocates nothing, and its address on the current device
+// (taken once per device with hipGetSymbolAddress).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void** out);
+
 // bf16 and fp8 inputs on the matrix cores (fp8 codes widen exactly to bf16).
 hipError_t launch_attn_mfma(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
                             hipStream_t st);

@@ -203,6 +203,30 @@ bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
                                      void* out, float* lse, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* Stage 3 for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, kernels and results as bslp_sparse_prefill_attn, with
+ * the workspace replaced by a device array inside the library of
+ * BSLP_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the first call on a
+ * device until the process ends.  Nothing is allocated or freed by the call.
+ * Arguments as bslp_sparse_prefill_attn, without workspace / workspace_bytes.
+ * Limits: the workspace bslp_get_sizes reports must fit the array; an
+ * automatic KV split count (kv_splits = 0) whose partial results would not
+ * fit falls back to no split, and any other overflow returns
+ * BSLP_ERR_UNSUPPORTED before anything is enqueued (kv_splits = 1 needs
+ * 6 * pooled_rows * Hkv * d bytes: 32 MiB covers 5.4M pooled (block, KV
+ * head) rows of 64 dims or 2.7M of 128).  Every call on one GPU shares its
+ * array, which keeps the last call's contents (nothing in it needs to start
+ * at zero); calls that overlap in time on one GPU race on it and must be
+ * serialised by the caller, e.g. by issuing them on one stream. */
+#define BSLP_NOALLOC_SCRATCH_BYTES (32u << 20)
+bslp_status bslp_sparse_prefill_attn_noalloc(const bslp_problem* problem,
+                                             const bslp_select_params* params, const void* q,
+                                             const void* k, const void* v, const float* kbar,
+                                             const float* vbar, const int32_t* cu,
+                                             const int32_t* idx, void* out, float* lse,
+                                             void* stream);
+
 /* Dense causal prefill attention on the same kernels, with no index stage:
  * every row attends to all keys j <= i of its request, as a
  * FlashAttention-style dense baseline against which the block-sparse path's

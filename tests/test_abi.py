@@ -225,3 +225,29 @@ def test_quantize_and_device_scales_validated_before_launch():
     st, d = _status(lambda: bslp.get_sizes(_problem(dtype="fp8", scales_dev=FakeTensor(ptr=0x4002))))
     assert st == 1 and "aligned" in d
     assert bslp.get_sizes(_problem(dtype="fp8", scales_dev=t)).total_tokens == 1300
+
+
+def test_noalloc_limits_checked_before_launch():
+    params = bslp.make_params(0.05)
+    t = FakeTensor()
+    # pooled copies alone: 6 * pooled_rows * Hkv * d bytes above 32 MiB
+    p = _problem(hq=8, hkv=8, head_dim=128, block_size=64, seqlens=[5462 * 64], kv_splits=1)
+    assert 6 * 5462 * 8 * 128 > bslp.NOALLOC_SCRATCH_BYTES
+    st, d = _status(lambda: bslp.sparse_prefill_attn_noalloc(p, params, t, t, t, t, t, t, t, t,
+                                                             stream=0))
+    assert st == 2 and "scratch" in d
+    # a requested split count whose partial results do not fit is refused too
+    p = _problem(hq=32, hkv=8, seqlens=[65536], kv_splits=4)
+    st, d = _status(lambda: bslp.sparse_prefill_attn_noalloc(p, params, t, t, t, t, t, t, t, t,
+                                                             stream=0))
+    assert st == 2 and "scratch" in d
+    # NULL tensors and bad problems are rejected as by the workspace entry point
+    st, _ = _status(lambda: bslp.sparse_prefill_attn_noalloc(_problem(), params, t, None, t, t,
+                                                             t, t, t, t, stream=0))
+    assert st == 1
+    st, _ = _status(lambda: bslp.sparse_prefill_attn_noalloc(_problem(head_dim=80), params, t,
+                                                             t, t, t, t, t, t, t, stream=0))
+    assert st == 2
+    # nothing to do for an empty problem: no scratch is touched
+    bslp.sparse_prefill_attn_noalloc(_problem(seqlens=[0]), params, None, None, None, None,
+                                     None, None, None, None, stream=0)
