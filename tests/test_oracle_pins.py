@@ -501,3 +501,127 @@ def test_unaligned_chunk_dense_rows_are_textbook_attention():
     for t in chunk["tiles"].values():
         assert np.allclose(t["O"], Od[t["pos"], t["heads"]], atol=1e-12)
         assert np.allclose(t["lse"], lsed[t["heads"], t["pos"]], atol=1e-12)
+
+
+# ---------------------------------------------------------------- FP8 attention arithmetic
+
+def _fp8_golden():
+    with open(os.path.join(HERE, "golden", "fp8_walk_tiny.json")) as f:
+        return json.load(f)
+
+
+def test_fp8_walk_golden_running_max():
+    """The e4m3 probabilities are rounded against the running maximum of a
+    backwards walk: hand-derived values (tests/golden/fp8_walk_tiny.json)."""
+    g = _fp8_golden()["walk"]
+    L, B = g["L"], g["B"]
+    k = np.zeros((L, 2))
+    k[:, 0] = -1000.0
+    for j, s in g["s"].items():
+        k[int(j), 0] = _num(s)
+    v = np.zeros((L, 2))
+    for j, val in g["v"].items():
+        v[int(j)] = val
+    kbar = oracle.pool_means(k[:, None], B)[:, 0]
+    vbar = oracle.pool_means(v[:, None], B)[:, 0]
+    q = np.array([[1.0, 0.0]])
+    O, lse = oracle.attend_rows_fp8([g["pos"]], q, k, v, kbar, vbar, g["sel"], g["todo"], B, 1.0,
+                                    1.0, 1.0)
+    np.testing.assert_allclose(O[0], [_num(x) for x in g["expected_O"]], atol=1e-13)
+    np.testing.assert_allclose(lse[0], _num(g["expected_lse"]), atol=1e-13)
+    # the exact arithmetic differs (LSE ln 2.8): the rounding is really applied
+    _, lse_x = oracle.attend_rows([g["pos"]], q, k, v, kbar, vbar, g["sel"], g["todo"], B, 1.0)
+    assert abs(lse_x[0] - math.log(2.8)) < 1e-12 and abs(lse[0] - lse_x[0]) > 1e-3
+
+
+def test_fp8_walk_golden_quantised_pooled_statistics():
+    g = _fp8_golden()["correction"]
+    L, B = g["L"], g["B"]
+    ck = float(g["k_scale"])
+    sc = math.log(2) / 4  # softmax scale
+    k = np.full((L, 2), 0.0)
+    k[g["pos"] + 1:, 0] = 1e3  # keys after the row are masked anyway
+    v = np.zeros((L, 2))
+    v[128] = g["v128"]
+    kbar = np.zeros((3, 2))
+    vbar = np.zeros((3, 2))
+    kbar[:2] = np.array(g["kbar_over_ck"], dtype=np.float64) * ck
+    vbar[:2] = _arr(g["vbar_over_cv"])
+    q = np.array([[1.0, 0.0]])
+    O, lse = oracle.attend_rows_fp8([g["pos"]], q, k, v, kbar, vbar, g["sel"], g["todo"], B, sc,
+                                    ck, 1.0)
+    np.testing.assert_allclose(O[0], [_num(x) for x in g["expected_O"]], atol=1e-12)
+    np.testing.assert_allclose(lse[0], math.log(7 / 4), atol=1e-12)
+    # unrounded pooled statistics would give other weights
+    O_x, _ = oracle.attend_rows([g["pos"]], q, k, v, kbar, vbar, g["sel"], g["todo"], B, sc)
+    assert np.abs(O_x[0] - O[0]).max() > 1e-2
+
+
+def test_fp8_walk_order():
+    """Steps of the walk: blocks backwards, a block's 64-key tiles descending,
+    the short last block clipped, then the correction chunks; split u takes
+    the CSR share [u c / U, (u + 1) c / U) and chunks u, u + U, ..."""
+    steps = oracle.walk([0, 3, 5], [1, 2, 64, 130], 128, 700)
+    got = [(kind, int(idx[0]), int(idx[-1])) if kind == "exact" else (kind, list(idx))
+           for kind, idx in steps]
+    assert got == [("exact", 640, 699), ("exact", 448, 511), ("exact", 384, 447),
+                   ("exact", 64, 127), ("exact", 0, 63),
+                   ("corr", [1, 2]), ("corr", [64]), ("corr", [130])]
+    s0 = [(k, int(i[0])) if k == "exact" else (k, list(i)) for k, i in
+          oracle.walk([0, 3, 5], [1, 2, 64, 130], 128, 700, 0, 2)]
+    s1 = [(k, int(i[0])) if k == "exact" else (k, list(i)) for k, i in
+          oracle.walk([0, 3, 5], [1, 2, 64, 130], 128, 700, 1, 2)]
+    assert s0 == [("exact", 64), ("exact", 0), ("corr", [1, 2]), ("corr", [130])]
+    assert s1 == [("exact", 640), ("exact", 448), ("exact", 384), ("corr", [64])]
+
+
+@pytest.mark.parametrize("B,n_splits,correction", [(64, 1, True), (128, 1, True), (128, 3, True),
+                                                   (64, 2, False), (128, 4, False)])
+def test_fp8_walk_exact_arithmetic_equals_attend_rows(B, n_splits, correction):
+    """With the rounding replaced by the identity, the walk, the running
+    rescale, the 2^8 offset, the split combine and the LSE correction must
+    reproduce plain block-sparse attention exactly."""
+    rng = np.random.default_rng(21 + B + n_splits)
+    L, d = 11 * B - 37, 8
+    N = -(-L // B)
+    k = rng.standard_normal((L, d)) * 1.5
+    v = rng.standard_normal((L, d))
+    kbar = oracle.pool_means(k[:, None], B)[:, 0]
+    vbar = oracle.pool_means(v[:, None], B)[:, 0]
+    I = N - 1
+    pos = np.arange(I * B, L)
+    q = rng.standard_normal((len(pos), d)) * 2
+    sel = [0, 2, 3, 7, I]
+    todo = oracle.todo_row(sel, I, correction)
+    O, lse = oracle.attend_rows_fp8(pos, q, k, v, kbar, vbar, sel, todo, B, 0.4, 0.7, 1.3,
+                                    n_splits=n_splits, quantize=lambda x: x)
+    O2, lse2 = oracle.attend_rows(pos, q, k, v, kbar, vbar, sel, todo, B, 0.4)
+    np.testing.assert_allclose(O, O2, atol=1e-12)
+    np.testing.assert_allclose(lse, lse2, atol=1e-12)
+
+
+def test_fp8_walk_probabilities_on_the_grid():
+    """Every rounded probability is an e4m3 value in [0, 256], so numerator
+    and l are sums of grid values; rounding only moves O within the e4m3
+    spacing of the weights."""
+    rng = np.random.default_rng(5)
+    L, B, d = 256, 64, 4
+    k = rng.standard_normal((L, d)) * 3
+    v = rng.standard_normal((L, d))
+    kbar = oracle.pool_means(k[:, None], B)[:, 0]
+    vbar = oracle.pool_means(v[:, None], B)[:, 0]
+    pos = np.arange(192, 256)
+    q = rng.standard_normal((64, d)) * 3
+    seen = []
+
+    def spy(x):
+        r = oracle.e4m3_round(x)
+        seen.append(r)
+        return r
+    O, _ = oracle.attend_rows_fp8(pos, q, k, v, kbar, vbar, [1, 3], [0, 2], B, 1.0, 1.0, 1.0,
+                                  quantize=spy)
+    probs = np.concatenate([s.ravel() for s in seen[2:]])  # after kbar, vbar
+    assert probs.max() <= 256 and probs.min() >= 0
+    np.testing.assert_array_equal(oracle.e4m3_round(probs), probs)
+    O2, _ = oracle.attend_rows(pos, q, k, v, kbar, vbar, [1, 3], [0, 2], B, 1.0)
+    assert np.abs(O - O2).max() < 0.25  # rounding error of 3-bit weights, not a wrong term
