@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbslp.so")
 
-SOURCES = ["api.cpp", "pool_scores.hip", "select.hip", "attn_valu.hip", "attn_mfma.hip", "scores_mfma.hip", "quant.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "pool_scores.hip", "select.hip", "attn_valu.hip", "attn_mfma.hip", "scores_mfma.hip", "quant.hip", "noalloc.hip", "attn_fp8.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -37,9 +37,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# The fp8 attention keeps every matrix-core accumulator in VGPRs: its 2- and
+# 4-wave instantiations would otherwise be given AGPR accumulators for the
+# fp8 MFMA, a form whose results read back wrong in an earlier version of
+# that kernel.
+FILE_FLAGS = {"attn_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

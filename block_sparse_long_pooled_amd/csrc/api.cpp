@@ -151,6 +151,15 @@ bslp_status hip_result(hipError_t e, const char* what) {
   return fail(BSLP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// float32 keeps exact fp32 arithmetic on the vector ALUs; bf16 runs on the
+// bf16 matrix cores; fp8 on the fp8 matrix cores with e4m3 probabilities.
+hipError_t launch_attn(const bslp::Plan& plan, const bslp::KVDesc& kv, int dtype,
+                       const bslp::AttnArgs& a, hipStream_t stream) {
+  if (dtype == BSLP_F32) return bslp::launch_attn_valu(plan, kv, dtype, a, stream);
+  if (dtype == BSLP_FP8_E4M3) return bslp::launch_attn_fp8(plan, kv, a, 0, stream);
+  return bslp::launch_attn_mfma(plan, kv, dtype, a, stream);
+}
+
 static_assert(BSLP_NOALLOC_SCRATCH_BYTES == bslp::kNoAllocScratchBytes,
               "the header states the device scratch size of the no-allocation entry point");
 
@@ -201,14 +210,7 @@ bslp_status sparse_attn(const bslp_problem* problem, const bslp_select_params* p
   bslp::AttnArgs a{q, k, v, kbar, vbar, cu, idx, out, lse, workspace,
                    problem->softmax_scale * host_scale(problem, 0), host_scale(problem, 1),
                    host_scale(problem, 2), sa.correction, 0, splits};
-  // bf16 and fp8 run on the matrix cores; float32 keeps exact fp32
-  // arithmetic on the vector ALUs.
-  const hipError_t e = problem->dtype == BSLP_F32
-                           ? bslp::launch_attn_valu(plan, kv, problem->dtype, a,
-                                                    (hipStream_t)stream)
-                           : bslp::launch_attn_mfma(plan, kv, problem->dtype, a,
-                                                    (hipStream_t)stream);
-  return hip_result(e, what);
+  return hip_result(launch_attn(plan, kv, problem->dtype, a, (hipStream_t)stream), what);
 }
 
 }  // namespace
@@ -296,12 +298,8 @@ bslp_status bslp_dense_prefill_attn(const bslp_problem* problem, const void* q, 
   bslp::AttnArgs a{q, k, v, nullptr, nullptr, nullptr, nullptr, out, lse, nullptr,
                    problem->softmax_scale * host_scale(problem, 0), host_scale(problem, 1),
                    host_scale(problem, 2), 0, 1, 1};
-  const hipError_t e = problem->dtype == BSLP_F32
-                           ? bslp::launch_attn_valu(plan, kv, problem->dtype, a,
-                                                    (hipStream_t)stream)
-                           : bslp::launch_attn_mfma(plan, kv, problem->dtype, a,
-                                                    (hipStream_t)stream);
-  return hip_result(e, "bslp_dense_prefill_attn");
+  return hip_result(launch_attn(plan, kv, problem->dtype, a, (hipStream_t)stream),
+                    "bslp_dense_prefill_attn");
 }
 
 bslp_status bslp_quantize_e4m3(int32_t src_dtype, const void* x, int64_t n, uint8_t* codes,

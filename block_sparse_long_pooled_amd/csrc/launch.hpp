@@ -55,6 +55,30 @@ size_t attn_workspace_bytes(const Plan& p, int splits);
 hipError_t launch_quantize_e4m3(int src_dtype, const void* x, int64_t n, uint8_t* codes,
                                 float* scale, hipStream_t st);
 
+// KV-split machinery shared by the matrix-core attention launchers: rows per
+// work unit, work-list length, the workspace regions of the partial results,
+// the work-list and merge launches, and the persistent grid size.
+int attn_rows_per_unit(const Plan& p);
+size_t attn_split_items(const Plan& p, int splits);
+struct SplitBufs {
+  float* part_o;   // [splits, T * Hq, d]
+  float* part_ml;  // [splits, T * Hq, 2]: (m in log2 units, l)
+  int32_t* items;  // work list
+  int* queue;      // [0] next item, [1] item count
+};
+SplitBufs split_bufs(const Plan& p, void* workspace, int splits);
+hipError_t launch_split_items(const Plan& pl, const int32_t* cu, int splits, int corr,
+                              int units_per_seg, const SplitBufs& b, hipStream_t st);
+hipError_t launch_split_merge(const Plan& p, const int32_t* cu, const SplitBufs& b, int splits,
+                              int corr, float lse_off, uint16_t* out, float* lse, hipStream_t st);
+hipError_t persistent_grid(const Plan& p, int splits, int per_cu, int64_t* grid);
+
+// fp8 inputs on the fp8 matrix cores (e4m3 probabilities, FlashPrefill V2 FP8
+// arithmetic); v_colmajor: V given as [Hkv, d, kv tokens] (contiguous) or
+// [pages, Hkv, d, page_size] (paged).
+hipError_t launch_attn_fp8(const Plan& p, const KVDesc& kv, const AttnArgs& a, int v_colmajor,
+                           hipStream_t st);
+
 // Size of the device array that serves as the attention workspace of the
 // entry point that allocates nothing, and its address on the current device
 // (taken once per device with hipGetSymbolAddress).

@@ -100,10 +100,17 @@ typedef struct bslp_problem {
    * and the scheduling paragraph after it: a work unit's
    * selected blocks are cut into contiguous shares balanced by count, each
    * run by its own workgroup, and the partial results are merged through
-   * their log-sum-exp).  0 = automatic (split only when the launch has fewer
-   * than about two workgroups per CU), 1 = never, 2..16 = that many splits.
-   * bf16 / fp8 only; the float32 path never splits.  It changes
-   * bslp_sizes.workspace_bytes. */
+   * their log-sum-exp).  1 = never, 2..16 = that many splits at most,
+   * 0 = automatic: with units = sum_b (N_b - i0_b) * Hkv * ceil(g B / R)
+   * work units of R = 256, 128 or 64 packed rows (the largest not above
+   * g B), a launch of fewer than 512 units in which some request has at
+   * least 16 blocks allows min(4, ceil(512 / units)) splits, any other
+   * launch none.  A segment with n selected blocks then uses
+   * max(1, min(allowed, steps / 24)) splits, steps = n B / 64 plus
+   * ceil(I / 64) when mean correction is on and I > 0; split u of U takes
+   * CSR positions [u n / U, (u + 1) n / U) and the correction chunks
+   * u, u + U, ... .  bf16 / fp8 only; the float32 path never splits.  It
+   * changes bslp_sizes.workspace_bytes. */
   int32_t kv_splits;
   /* fp8 only: DEVICE float[3] = (q_scale, k_scale, v_scale), as written by
    * bslp_quantize_e4m3, or NULL to use the host floats above (then ignored).
@@ -188,6 +195,21 @@ bslp_status bslp_select_blocks(const bslp_problem* problem, const bslp_select_pa
  *   correction   if params->mean_correction: for every J <= I-1 not in Sel_I,
  *                c_J = softmax_scale * q . kbar_J + ln|B_J| with value vbar_J;
  *   O = sum softmax weights * values, LSE = m + ln l (natural log).
+ * Walk: each segment's selected blocks are taken from the last to the
+ * first, each in 64-key tiles from the highest to the lowest, then the
+ * correction terms in chunks of 64 pooled blocks (CSR paragraph; tile
+ * configuration paragraph).  bf16 and float32 results depend on it only
+ * through rounding.
+ * fp8 arithmetic (FP8 paragraph; Tab. 8 paragraph): with c_q, c_k, c_v the
+ * per-tensor scales, logits are softmax_scale c_q c_k (Q~ K~^T), computed
+ * exactly on the bf16 matrix cores; m is the exact running row maximum of
+ * the walk; each probability is rounded to e4m3 as P~ = e4m3(2^8 exp(s - m))
+ * (nearest even) and O = c_v (P~ V~) / l with l = sum P~, on the fp8 matrix
+ * cores; LSE = m + ln l - 8 ln 2.  The correction terms use the pooled
+ * statistics rounded the same way: e4m3 of the exact mean of each block's K
+ * (V) codes, computed from k and v themselves (kbar and vbar are not read
+ * for fp8).  A probability within about 1e-5 of an e4m3 rounding midpoint
+ * may round either way.
  * out: [T, Hq, d], float32 for BSLP_F32 else bfloat16.  lse: float32
  * [Hq, T] or NULL.  A row that sees no key gets O = 0 and LSE = -inf.
  * kbar / vbar / cu / idx are the outputs of stages 1 and 2 for the same

@@ -52,6 +52,7 @@ class GpuResult:
     out: np.ndarray
     lse: np.ndarray
     ms: float = 0.0
+    kv_splits: int = 0  # the launch's kv_splits request (0: automatic)
 
 
 def to_device(inp):
@@ -92,7 +93,7 @@ def run_gpu(w: Workload, inp, alpha=None, correction=None, dev_tensors=None,
     ms = (time.time() - t0) * 1e3
     c = lambda t: t.cpu().numpy()
     res = GpuResult(c(bufs.kbar), c(bufs.vbar), c(bufs.scores), c(bufs.counts), c(bufs.cu),
-                    c(bufs.idx), c(bufs.out.float()), c(bufs.lse), ms)
+                    c(bufs.idx), c(bufs.out.float()), c(bufs.lse), ms, kv_splits)
     if check:
         check_arrays(w, res)
     return res
@@ -156,6 +157,8 @@ class Report:
         self.kbar_err = 0.0
         self.out_err = 0.0
         self.lse_err = 0.0
+        self.exact_err = 0.0  # fp8: output against exact (unrounded) arithmetic, not gated
+        self.tie_rows = 0     # fp8: rows matched with another rounding of a near tie
         self.blocks = 0
         self.selected = 0
 
@@ -165,14 +168,87 @@ class Report:
         self.band += o.band
         self.blocks += o.blocks
         self.selected += o.selected
-        for f in ("score_rel", "kbar_err", "out_err", "lse_err"):
+        self.tie_rows += o.tie_rows
+        for f in ("score_rel", "kbar_err", "out_err", "lse_err", "exact_err"):
             setattr(self, f, max(getattr(self, f), getattr(o, f)))
 
     def __str__(self):
         return (f"tiles={self.tiles} sel_mismatch={self.sel_mismatch} band={self.band} "
                 f"score_rel={self.score_rel:.2e} pooled_err={self.kbar_err:.2e} "
                 f"out_maxabs={self.out_err:.3e} lse_maxabs={self.lse_err:.3e} "
-                f"density={self.selected / max(1, self.blocks):.4f}")
+                f"density={self.selected / max(1, self.blocks):.4f}" +
+                (f" out_vs_exact={self.exact_err:.3e} tie_rows={self.tie_rows}"
+                 if self.exact_err else ""))
+
+
+def launch_split_allowance(w: Workload, kv_splits: int) -> int:
+    """KV splits a launch allows, by the rule bslp.h documents for
+    bslp_problem.kv_splits: 1 for float32 or kv_splits = 1; kv_splits when
+    2..16; automatic (0): when the launch has fewer than 512 work units (of
+    256, 128 or 64 packed rows) and some request has at least 16 blocks,
+    ceil(512 / units) capped at 4, else 1."""
+    if w.dtype == "f32" or kv_splits == 1:
+        return 1
+    if kv_splits >= 2:
+        return kv_splits
+    rows = w.g * w.block
+    per_unit = 256 if rows >= 256 else 128 if rows >= 128 else 64
+    ups = -(-rows // per_unit)
+    tiles = 0
+    max_n = 0
+    for L, Lq in zip(w.seqlens, w.query_lens):
+        N = -(-L // w.block)
+        i0 = (L - Lq) // w.block if Lq else N
+        tiles += N - i0
+        max_n = max(max_n, N)
+    units = tiles * w.hkv * ups
+    if units == 0 or units >= 512 or max_n < 16:
+        return 1
+    return min(4, -(-512 // units))
+
+
+def segment_splits(n_sel: int, I: int, B: int, correction: bool, allowance: int) -> int:
+    """Splits of one segment (bslp.h): one per 24 steps of work, its selected
+    blocks in 64-key tiles plus its correction chunks, at most `allowance`."""
+    steps = n_sel * (B // 64) + ((I + 63) // 64 if correction and I > 0 else 0)
+    return max(1, min(allowance, steps // 24))
+
+
+# A probability within this relative distance of an e4m3 rounding midpoint may
+# round either way on the GPU: its logits carry float32 rounding (values up
+# to about 2^7 in log2 units, an ulp of 7.6e-6, so P moves by about 5e-6),
+# the matrix cores' float32 accumulation and v_exp_f32's last-bit error.
+# 1e-4 is twenty times that.  Both roundings are correct results.
+FP8_TIE_BAND = 1e-4
+
+
+def _resolve_ties(w, rv, pos, rows, k_h, v_h, sel, todo, ns, go, gl, O, lse, near, rep):
+    """Rows whose GPU output misses the oracle's and that hold near-tie
+    probabilities are compared with the oracle's other roundings of those
+    (at most the 3 heaviest, every subset); the closest is kept."""
+    import itertools
+    tol = out_tol(w.dtype)
+    err = np.abs(go - O).max(axis=1)
+    fin = np.isfinite(lse)
+    lerr = np.where(fin, np.abs(np.where(fin, gl - lse, 0.0)), 0.0)
+    O, lse = O.copy(), lse.copy()
+    for r in np.nonzero((err > tol) | (lerr > 2e-2))[0]:
+        if not near[r]:
+            continue
+        keys = near[r][-3:]
+        best = (err[r], O[r], lse[r])
+        for n in range(1, len(keys) + 1):
+            for sub in itertools.combinations(keys, n):
+                Or, lr = oracle.attend_rows_fp8([pos[r]], rows[r:r + 1], k_h, v_h, sel, todo,
+                                                w.block, w.scale, rv.ks, rv.vs, n_splits=ns,
+                                                flips={(0, key) for key in sub})
+                e = float(np.abs(go[r] - Or[0]).max())
+                if e < best[0]:
+                    best = (e, Or[0], lr[0])
+        if best[0] < err[r]:
+            O[r], lse[r] = best[1], best[2]
+            rep.tie_rows += 1
+    return O, lse
 
 
 def _tile_check(w, rv, b, h, I, s, off, g: GpuResult, alpha, corr, pb, rep: Report):
@@ -208,8 +284,24 @@ def _tile_check(w, rv, b, h, I, s, off, g: GpuResult, alpha, corr, pb, rep: Repo
     rep.blocks += I + 1
     rep.selected += len(sel_g)
     todo = oracle.todo_row(sel_g, I, corr)
-    O, lse = oracle.attend_rows(pos, rows, k_h, v_h, kbar_h, vbar_h, sel_g, todo, w.block,
-                                w.scale)
+    if w.dtype == "fp8":
+        # the FP8 arithmetic of the pages (e4m3 probabilities against the
+        # running maximum of the walk, quantised pooled statistics), over the
+        # splits the launch gave this segment
+        ns = segment_splits(len(sel_g), I, w.block, corr,
+                            launch_split_allowance(w, g.kv_splits))
+        O, lse, near = oracle.attend_rows_fp8(pos, rows, k_h, v_h, sel_g, todo, w.block, w.scale,
+                                              rv.ks, rv.vs, n_splits=ns, tie_band=FP8_TIE_BAND)
+        go = g.out[rv.qstart + pos - rv.q_off, heads]
+        gl = g.lse[heads, rv.qstart + pos - rv.q_off]
+        O, lse = _resolve_ties(w, rv, pos, rows, k_h, v_h, sel_g, todo, ns, go, gl, O, lse, near,
+                               rep)
+        Ox, _ = oracle.attend_rows(pos, rows, k_h, v_h, kbar_h, vbar_h, sel_g, todo, w.block,
+                                   w.scale)
+        rep.exact_err = max(rep.exact_err, float(np.abs(go - Ox).max()))
+    else:
+        O, lse = oracle.attend_rows(pos, rows, k_h, v_h, kbar_h, vbar_h, sel_g, todo, w.block,
+                                    w.scale)
     go = g.out[rv.qstart + pos - rv.q_off, heads]
     gl = g.lse[heads, rv.qstart + pos - rv.q_off]
     rep.out_err = max(rep.out_err, float(np.abs(go - O).max()))
@@ -433,5 +525,6 @@ def dense_flops(w: Workload) -> float:
 
 
 __all__ = ["GpuResult", "Report", "assert_parity", "check_arrays", "compare",
+           "launch_split_allowance", "segment_splits",
            "compare_selection", "dense_flops", "log", "make_inputs", "oracle_score_rows",
            "run_gpu", "sample_tiles", "segment_arrays", "segments", "to_device", "math"]

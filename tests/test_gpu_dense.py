@@ -2,8 +2,9 @@
 j <= i, no index stage) against the fp64 oracle, through the C ABI.
 
 Bar: output max-abs <= 2e-3 (fp32) / 2e-2 (bf16, fp8) and LSE max-abs <= 1e-3
-(fp32) / 2e-2 against the textbook dense attention; bit-identical to the
-sparse path with every block selected and mean correction off."""
+(fp32) / 2e-2 against the textbook dense attention (fp8: the oracle's FP8
+arithmetic over every causal block); bit-identical to the sparse path with
+every block selected and mean correction off."""
 import numpy as np
 import pytest
 
@@ -63,6 +64,18 @@ def test_dense_matches_textbook(w):
     err_o = err_l = 0.0
     for b, L in enumerate(w.seqlens):
         rv = RequestView(w, inp, b)
+        if w.dtype == "fp8":
+            # the pages' FP8 arithmetic over every causal block, tile by tile
+            for h in range(w.hkv):
+                k_h, v_h, kbar_h, vbar_h = rv.head(h)
+                for I in range(-(-L // w.block)):
+                    pos, heads, rows = oracle.tile_query_rows(rv.q, h, w.g, w.block, I)
+                    O, l = oracle.attend_rows_fp8(pos, rows, k_h, v_h, list(range(I + 1)), [],
+                                                  w.block, w.scale, rv.ks, rv.vs)
+                    err_o = max(err_o, float(np.abs(out[start + pos, heads] - O).max()))
+                    err_l = max(err_l, float(np.abs(lse[heads, start + pos] - l).max()))
+            start += L
+            continue
         k = np.stack([rv.head(h)[0] for h in range(w.hkv)], axis=1)
         v = np.stack([rv.head(h)[1] for h in range(w.hkv)], axis=1)
         Od, lsed = oracle.dense_causal_reference(rv.q, k, v, w.scale)

@@ -3,8 +3,8 @@ contiguous shares balanced by count, partial results merged through their
 LSE) against the fp64 oracle, through the C ABI.
 
 Bar: as the unsplit path (selections bit-exact outside the band, outputs
-<= 2e-2 for bf16 / fp8 against the oracle); the split result also agrees with
-the unsplit one to within 2e-2 or one bf16 spacing of the value, whichever is
+<= 2e-2 for bf16 / fp8 against the oracle, whose fp8 arithmetic walks the
+same splits); a bf16 split result also agrees with the unsplit one to within 2e-2 or one bf16 spacing of the value, whichever is
 larger: two float32 results on either side of a rounding midpoint round to
 neighbouring bf16 outputs, 2^-5 apart at |O| in [4, 8)."""
 import numpy as np
@@ -59,7 +59,8 @@ def test_forced_splits_match_oracle(w, splits):
     # the heavy segments did split: their rounding differs from the whole walk
     g = run_gpu(w, inp, correction=True, dev_tensors=dev, kv_splits=splits)
     assert not np.array_equal(g.out, whole.out)
-    assert runs_agree(g.out, whole.out)
+    if w.dtype != "fp8":  # fp8 splits round P~ against their own maxima (oracle above)
+        assert runs_agree(g.out, whole.out)
 
 
 @pytest.mark.parametrize("alpha", [0.05, 0.0])
