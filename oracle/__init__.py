@@ -24,10 +24,10 @@ from .flashprefill import (attend_rows, block_scores_row, dense_causal_reference
                            pool_means, request_oracle, select_row, tile_query_rows,
                            todo_row, wasted_row_fraction)
 from .fp8 import decode_e4m3fn, encode_e4m3fn, quantize_per_tensor
-from .fp8_attention import attend_rows_fp8, e4m3_round, walk
+from .fp8_attention import attend_rows_fp8, e4m3_round, pooled_code_means, walk
 
 __all__ = ["attend_rows", "block_scores_row", "dense_causal_reference", "forced_blocks",
            "merge_partials", "n_blocks", "packgqa_rows", "pool_means", "request_oracle",
            "select_row", "tile_query_rows", "todo_row", "wasted_row_fraction",
            "decode_e4m3fn", "encode_e4m3fn", "quantize_per_tensor", "attend_rows_fp8",
-           "e4m3_round", "walk"]
+           "e4m3_round", "pooled_code_means", "walk"]

@@ -29,7 +29,7 @@ def encode_e4m3fn(x) -> np.ndarray:
     magnitudes above the largest finite value 448 saturated to it.  Written
     from the format: the representable magnitudes are enumerated from the
     field definitions above and each input picks the closest one."""
-    mags = np.array([decode_e4m3fn(c) for c in range(0x7F)], dtype=np.float64)  # 0 .. 448
+    mags = _MAGNITUDES
     a = np.minimum(np.abs(np.asarray(x, dtype=np.float64)), 448.0)
     # index of the largest representable magnitude <= a, and the next one up
     lo = np.searchsorted(mags, a, side="right") - 1
@@ -56,3 +56,7 @@ def quantize_per_tensor(x) -> tuple:
     scale = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
     q = (xf / scale).astype(np.float32)
     return encode_e4m3fn(q), scale
+
+
+# every non-negative finite e4m3 magnitude, in code order (0 .. 448)
+_MAGNITUDES = np.array([decode_e4m3fn(c) for c in range(0x7F)], dtype=np.float64)

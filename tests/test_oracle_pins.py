@@ -525,8 +525,7 @@ def test_fp8_walk_golden_running_max():
     kbar = oracle.pool_means(k[:, None], B)[:, 0]
     vbar = oracle.pool_means(v[:, None], B)[:, 0]
     q = np.array([[1.0, 0.0]])
-    O, lse = oracle.attend_rows_fp8([g["pos"]], q, k, v, kbar, vbar, g["sel"], g["todo"], B, 1.0,
-                                    1.0, 1.0)
+    O, lse = oracle.attend_rows_fp8([g["pos"]], q, k, v, g["sel"], g["todo"], B, 1.0, 1.0, 1.0)
     np.testing.assert_allclose(O[0], [_num(x) for x in g["expected_O"]], atol=1e-13)
     np.testing.assert_allclose(lse[0], _num(g["expected_lse"]), atol=1e-13)
     # the exact arithmetic differs (LSE ln 2.8): the rounding is really applied
@@ -539,22 +538,65 @@ def test_fp8_walk_golden_quantised_pooled_statistics():
     L, B = g["L"], g["B"]
     ck = float(g["k_scale"])
     sc = math.log(2) / 4  # softmax scale
-    k = np.full((L, 2), 0.0)
+    k = np.zeros((L, 2))
     k[g["pos"] + 1:, 0] = 1e3  # keys after the row are masked anyway
     v = np.zeros((L, 2))
     v[128] = g["v128"]
-    kbar = np.zeros((3, 2))
-    vbar = np.zeros((3, 2))
-    kbar[:2] = np.array(g["kbar_over_ck"], dtype=np.float64) * ck
-    vbar[:2] = _arr(g["vbar_over_cv"])
+    for J in (0, 1):
+        keys, vals = _arr(g[f"block{J}_keys"]), _arr(g[f"block{J}_values"])
+        for half in (0, 1):
+            rows = slice(J * B + 32 * half, J * B + 32 * half + 32)
+            k[rows] = keys[half] * ck
+            v[rows] = vals[half]
     q = np.array([[1.0, 0.0]])
-    O, lse = oracle.attend_rows_fp8([g["pos"]], q, k, v, kbar, vbar, g["sel"], g["todo"], B, sc,
-                                    ck, 1.0)
+    O, lse = oracle.attend_rows_fp8([g["pos"]], q, k, v, g["sel"], g["todo"], B, sc, ck, 1.0)
     np.testing.assert_allclose(O[0], [_num(x) for x in g["expected_O"]], atol=1e-12)
     np.testing.assert_allclose(lse[0], math.log(7 / 4), atol=1e-12)
     # unrounded pooled statistics would give other weights
+    kbar = oracle.pool_means(k[:, None], B)[:, 0]
+    vbar = oracle.pool_means(v[:, None], B)[:, 0]
     O_x, _ = oracle.attend_rows([g["pos"]], q, k, v, kbar, vbar, g["sel"], g["todo"], B, sc)
     assert np.abs(O_x[0] - O[0]).max() > 1e-2
+
+
+def test_fp8_pooled_code_means_are_exact():
+    """Block means of the codes are recovered exactly from code * scale, so a
+    mean that sits on an e4m3 midpoint is a true tie (rounded to even)."""
+    rng = np.random.default_rng(3)
+    codes = oracle.decode_e4m3fn(rng.integers(0, 0x7E, size=(256, 4)).astype(np.uint8))
+    scale = 0.0123456789
+    means = oracle.pooled_code_means(codes * scale, scale, 64)
+    exact = np.stack([codes[i * 64:(i + 1) * 64].mean(axis=0) for i in range(4)])
+    np.testing.assert_array_equal(means, exact)
+    # a block of 32 codes 28 and 32 codes 30: mean 29, the midpoint of 28 and 30
+    block = np.array([[28.0]] * 32 + [[30.0]] * 32)
+    m = oracle.pooled_code_means(block * 0.37, 0.37, 64)
+    assert m[0, 0] == 29.0 and oracle.e4m3_round(m)[0, 0] == 28.0
+
+
+def test_fp8_near_tie_flip_changes_one_rounding():
+    """A probability within the tie band is reported, and forcing its other
+    rounding changes the result by that one weight (the golden walk: key 65
+    has P = 76.8, not near a midpoint; with a wide band it is reported)."""
+    g = _fp8_golden()["walk"]
+    L, B = g["L"], g["B"]
+    k = np.zeros((L, 2))
+    k[:, 0] = -1000.0
+    for j, s in g["s"].items():
+        k[int(j), 0] = _num(s)
+    v = np.zeros((L, 2))
+    for j, val in g["v"].items():
+        v[int(j)] = val
+    q = np.array([[1.0, 0.0]])
+    O0, l0, near = oracle.attend_rows_fp8([g["pos"]], q, k, v, g["sel"], g["todo"], B, 1.0, 1.0,
+                                          1.0, tie_band=0.05)
+    assert 65 in near[0]  # 76.8 is 0.8 from the midpoint 76 (1%)
+    O1, l1 = oracle.attend_rows_fp8([g["pos"]], q, k, v, g["sel"], g["todo"], B, 1.0, 1.0, 1.0,
+                                    flips={(0, 65)})
+    # key 65 rounds to 72 instead of 80 in the first step (then rescaled by
+    # 1/1.5): l = 328 / 1.5 + 256 = 1424/3
+    np.testing.assert_allclose(O1[0], [912 / 1424, 656 / 1424], atol=1e-12)
+    assert abs(l1[0] - l0[0]) > 1e-3
 
 
 def test_fp8_walk_order():
@@ -584,8 +626,9 @@ def test_fp8_walk_exact_arithmetic_equals_attend_rows(B, n_splits, correction):
     rng = np.random.default_rng(21 + B + n_splits)
     L, d = 11 * B - 37, 8
     N = -(-L // B)
-    k = rng.standard_normal((L, d)) * 1.5
-    v = rng.standard_normal((L, d))
+    # e4m3 codes times the per-tensor scales, as the fp8 inputs are
+    k = oracle.e4m3_round(rng.standard_normal((L, d)) * 30) * 0.7 / 30
+    v = oracle.e4m3_round(rng.standard_normal((L, d)) * 60) * 1.3 / 60
     kbar = oracle.pool_means(k[:, None], B)[:, 0]
     vbar = oracle.pool_means(v[:, None], B)[:, 0]
     I = N - 1
@@ -593,7 +636,7 @@ def test_fp8_walk_exact_arithmetic_equals_attend_rows(B, n_splits, correction):
     q = rng.standard_normal((len(pos), d)) * 2
     sel = [0, 2, 3, 7, I]
     todo = oracle.todo_row(sel, I, correction)
-    O, lse = oracle.attend_rows_fp8(pos, q, k, v, kbar, vbar, sel, todo, B, 0.4, 0.7, 1.3,
+    O, lse = oracle.attend_rows_fp8(pos, q, k, v, sel, todo, B, 0.4, 0.7 / 30, 1.3 / 60,
                                     n_splits=n_splits, quantize=lambda x: x)
     O2, lse2 = oracle.attend_rows(pos, q, k, v, kbar, vbar, sel, todo, B, 0.4)
     np.testing.assert_allclose(O, O2, atol=1e-12)
@@ -618,8 +661,7 @@ def test_fp8_walk_probabilities_on_the_grid():
         r = oracle.e4m3_round(x)
         seen.append(r)
         return r
-    O, _ = oracle.attend_rows_fp8(pos, q, k, v, kbar, vbar, [1, 3], [0, 2], B, 1.0, 1.0, 1.0,
-                                  quantize=spy)
+    O, _ = oracle.attend_rows_fp8(pos, q, k, v, [1, 3], [0, 2], B, 1.0, 1.0, 1.0, quantize=spy)
     probs = np.concatenate([s.ravel() for s in seen[2:]])  # after kbar, vbar
     assert probs.max() <= 256 and probs.min() >= 0
     np.testing.assert_array_equal(oracle.e4m3_round(probs), probs)
