@@ -76,7 +76,8 @@ class Sizes(ctypes.Structure):
     ]
 
 
-EXPORTS = ("bslp_get_sizes", "bslp_block_scores", "bslp_select_blocks",
+EXPORTS = ("bslp_get_sizes", "bslp_block_scores", "bslp_pool_kv", "bslp_score_blocks",
+           "bslp_select_blocks",
            "bslp_sparse_prefill_attn", "bslp_sparse_prefill_attn_noalloc",
            "bslp_dense_prefill_attn", "bslp_quantize_e4m3", "bslp_status_string",
            "bslp_last_error")
@@ -98,6 +99,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp = ctypes.c_void_p
     lib.bslp_get_sizes.argtypes = [P(Problem), P(Sizes)]
     lib.bslp_block_scores.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, vp]
+    lib.bslp_pool_kv.argtypes = [P(Problem), vp, vp, vp, vp, vp]
+    lib.bslp_score_blocks.argtypes = [P(Problem), vp, vp, vp, vp]
     lib.bslp_select_blocks.argtypes = [P(Problem), P(SelectParams), vp, vp, vp, vp, vp]
     lib.bslp_sparse_prefill_attn.argtypes = [P(Problem), P(SelectParams), vp, vp, vp, vp, vp,
                                              vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -105,7 +108,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                      vp, vp, vp, vp, vp, vp, vp]
     lib.bslp_dense_prefill_attn.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp]
     lib.bslp_quantize_e4m3.argtypes = [ctypes.c_int32, vp, ctypes.c_int64, vp, vp, vp]
-    for name in ("bslp_get_sizes", "bslp_block_scores", "bslp_select_blocks",
+    for name in ("bslp_get_sizes", "bslp_block_scores", "bslp_pool_kv", "bslp_score_blocks",
+                 "bslp_select_blocks",
                  "bslp_sparse_prefill_attn", "bslp_sparse_prefill_attn_noalloc",
                  "bslp_dense_prefill_attn", "bslp_quantize_e4m3"):
         getattr(lib, name).restype = ctypes.c_int
@@ -189,6 +193,18 @@ def block_scores(problem, q, k, v, kbar, vbar, scores, stream=None):
                                             _stream(stream)))
 
 
+def pool_kv(problem, k, v, kbar, vbar, stream=None):
+    """The pooling half of block_scores."""
+    _check(load_library().bslp_pool_kv(ctypes.byref(problem), _ptr(k), _ptr(v), _ptr(kbar),
+                                       _ptr(vbar), _stream(stream)))
+
+
+def score_blocks(problem, q, kbar, scores, stream=None):
+    """The scoring half of block_scores (kbar from pool_kv)."""
+    _check(load_library().bslp_score_blocks(ctypes.byref(problem), _ptr(q), _ptr(kbar),
+                                            _ptr(scores), _stream(stream)))
+
+
 def select_blocks(problem, params, scores, counts, cu, idx, stream=None):
     _check(load_library().bslp_select_blocks(ctypes.byref(problem), ctypes.byref(params),
                                              _ptr(scores), _ptr(counts), _ptr(cu), _ptr(idx),
@@ -267,4 +283,4 @@ def prefill(problem, params, q, k, v, bufs: Buffers | None = None, stream=None) 
 __all__ = ["BF16", "F32", "FP8_E4M3", "BslpError", "Buffers", "EXPORTS", "LIB_PATH", "Problem",
            "SelectParams", "Sizes", "block_scores", "dense_prefill_attn", "get_sizes",
            "load_library", "make_params",
-           "make_problem", "prefill", "quantize_e4m3", "select_blocks", "sparse_prefill_attn", "sparse_prefill_attn_noalloc"]
+           "make_problem", "pool_kv", "prefill", "quantize_e4m3", "score_blocks", "select_blocks", "sparse_prefill_attn", "sparse_prefill_attn_noalloc"]

@@ -246,8 +246,40 @@ bslp_status bslp_block_scores(const bslp_problem* problem, const void* q, const 
   return hip_result(bslp::launch_stage1(plan, kv, problem->dtype, q, k, v, host_scale(problem, 0),
                                         host_scale(problem, 1), host_scale(problem, 2),
                                         problem->softmax_scale, kbar, vbar, scores,
+                                        bslp::kStagePool | bslp::kStageScores,
                                         (hipStream_t)stream),
                     "bslp_block_scores");
+}
+
+bslp_status bslp_pool_kv(const bslp_problem* problem, const void* k, const void* v, float* kbar,
+                         float* vbar, void* stream) {
+  bslp::Plan plan;
+  bslp::KVDesc kv;
+  bslp_status st = build_plan(problem, &plan, &kv);
+  if (st != BSLP_OK) return st;
+  if (plan.pooled_rows == 0) return BSLP_OK;
+  if (!k || !v || !kbar || !vbar) return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  return hip_result(bslp::launch_stage1(plan, kv, problem->dtype, nullptr, k, v,
+                                        host_scale(problem, 0), host_scale(problem, 1),
+                                        host_scale(problem, 2), problem->softmax_scale, kbar, vbar,
+                                        nullptr, bslp::kStagePool, (hipStream_t)stream),
+                    "bslp_pool_kv");
+}
+
+bslp_status bslp_score_blocks(const bslp_problem* problem, const void* q, const float* kbar,
+                              float* scores, void* stream) {
+  bslp::Plan plan;
+  bslp::KVDesc kv;
+  bslp_status st = build_plan(problem, &plan, &kv);
+  if (st != BSLP_OK) return st;
+  if (plan.total_tokens == 0) return BSLP_OK;
+  if (!q || !kbar || !scores) return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  return hip_result(bslp::launch_stage1(plan, kv, problem->dtype, q, nullptr, nullptr,
+                                        host_scale(problem, 0), host_scale(problem, 1),
+                                        host_scale(problem, 2), problem->softmax_scale,
+                                        const_cast<float*>(kbar), nullptr, scores,
+                                        bslp::kStageScores, (hipStream_t)stream),
+                    "bslp_score_blocks");
 }
 
 bslp_status bslp_select_blocks(const bslp_problem* problem, const bslp_select_params* params,

@@ -25,10 +25,13 @@ struct AttnArgs {
   int splits;  // KV splits per work unit (1: none), from attn_splits
 };
 
+// Stage 1: pooling (kStagePool) and / or block scores (kStageScores).
+constexpr int kStagePool = 1;
+constexpr int kStageScores = 2;
 hipError_t launch_stage1(const Plan& p, const KVDesc& kv, int dtype, const void* q, const void* k,
                          const void* v, float q_scale, float k_scale, float v_scale,
                          float softmax_scale, float* kbar, float* vbar, float* scores,
-                         hipStream_t st);
+                         int parts, hipStream_t st);
 
 // Block scores on the matrix cores (bf16 / fp8 inputs, g*B <= 1024 rows per
 // tile); c2 = softmax_scale * q_scale * log2(e).

@@ -233,9 +233,9 @@ template <int DT, int D>
 static hipError_t launch_stage1_t(const Plan& p, const KVDesc& kv, const void* q, const void* k,
                                   const void* v, float q_scale, float k_scale, float v_scale,
                                   float softmax_scale, float* kbar, float* vbar, float* scores,
-                                  hipStream_t st) {
+                                  int parts, hipStream_t st) {
   using T = typename Elem<DT>::T;
-  if (p.pooled_rows > 0) {
+  if ((parts & kStagePool) && p.pooled_rows > 0) {
     const int groups = (p.hkv + pool_heads<D>() - 1) / pool_heads<D>();
     dim3 grid((unsigned)p.pooled_rows, (unsigned)groups, 2);
     hipLaunchKernelGGL((pool_kernel<DT, D>), grid, dim3(kPoolThreads), 0, st, p, kv, (const T*)k,
@@ -243,6 +243,7 @@ static hipError_t launch_stage1_t(const Plan& p, const KVDesc& kv, const void* q
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (!(parts & kStageScores)) return hipSuccess;
   if (p.num_segments > 0 && scores_mfma_supported(p, DT)) {
     const double c2 = (double)softmax_scale * (double)q_scale * 1.4426950408889634;
     return launch_scores_mfma(p, DT, q, kbar, (float)c2, scores, st);
@@ -261,10 +262,10 @@ static hipError_t launch_stage1_t(const Plan& p, const KVDesc& kv, const void* q
 hipError_t launch_stage1(const Plan& p, const KVDesc& kv, int dtype, const void* q, const void* k,
                          const void* v, float q_scale, float k_scale, float v_scale,
                          float softmax_scale, float* kbar, float* vbar, float* scores,
-                         hipStream_t st) {
+                         int parts, hipStream_t st) {
 #define BSLP_S1(DT, D) \
   return launch_stage1_t<DT, D>(p, kv, q, k, v, q_scale, k_scale, v_scale, softmax_scale, kbar, \
-                                vbar, scores, st)
+                                vbar, scores, parts, st)
   if (p.d == 128) {
     if (dtype == kF32) BSLP_S1(kF32, 128);
     if (dtype == kBF16) BSLP_S1(kBF16, 128);

@@ -173,6 +173,17 @@ bslp_status bslp_block_scores(const bslp_problem* problem, const void* q, const 
                               const void* v, float* kbar, float* vbar, float* scores,
                               void* stream);
 
+/* The two halves of bslp_block_scores, for callers that time or overlap
+ * them separately; together they enqueue exactly the launches of
+ * bslp_block_scores.
+ * bslp_pool_kv: the pooled means kbar, vbar from k, v (as above).
+ * bslp_score_blocks: the score rows from q and the kbar of bslp_pool_kv for
+ *   the same problem.  Errors as bslp_block_scores. */
+bslp_status bslp_pool_kv(const bslp_problem* problem, const void* k, const void* v, float* kbar,
+                         float* vbar, void* stream);
+bslp_status bslp_score_blocks(const bslp_problem* problem, const void* q, const float* kbar,
+                              float* scores, void* stream);
+
 /* Stage 2: selection (FlashPrefill V2, Sec. 3.1 threshold paragraph and the
  * CSR paragraph; threshold formula printed on the FlashPrefill summary page).
  *   thresh_I = alpha * max_{J<=I} Score_IJ;

@@ -143,6 +143,27 @@ def test_varlen_equals_standalone_bitwise(kv_splits):
         assert np.array_equal(gb.lse, g.lse[:, sl], equal_nan=True)
 
 
+def test_pool_and_score_halves_equal_block_scores():
+    # bslp_pool_kv + bslp_score_blocks enqueue exactly bslp_block_scores' work
+    import torch
+
+    import block_sparse_long_pooled_amd as bslp
+    for w in (Workload("halves-bf16", (900, 300), 8, 2, 128, 128, "bf16", attractors=4),
+              Workload("halves-fp8-paged", (700,), 8, 2, 64, 64, "fp8", page_size=16)):
+        inp = make_inputs(w, 4)
+        q, k, v, table = to_device(inp)
+        prob = bslp.make_problem(w.dtype, w.hq, w.hkv, w.d, w.block, w.seqlens,
+                                 q_scale=inp.q_scale, k_scale=inp.k_scale, v_scale=inp.v_scale,
+                                 page_table=table, page_size=w.page_size)
+        a, b = bslp.Buffers(prob), bslp.Buffers(prob)
+        bslp.block_scores(prob, q, k, v, a.kbar, a.vbar, a.scores)
+        bslp.pool_kv(prob, k, v, b.kbar, b.vbar)
+        bslp.score_blocks(prob, q, b.kbar, b.scores)
+        torch.cuda.synchronize()
+        for n in ("kbar", "vbar", "scores"):
+            assert torch.equal(getattr(a, n), getattr(b, n)), (w.name, n)
+
+
 def test_deterministic_bitwise():
     w = GQA_BF16_16K.replace(seqlens=(4096,))
     inp = make_inputs(w, 0)
