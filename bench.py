@@ -189,7 +189,7 @@ def stage_bytes_flops(w, sizes) -> dict:
     pool: K and V read once, K-bar and V-bar written (float32).
     scores: Q read once, K-bar read once, the score rows written; on the
     matrix cores every (row, pooled key) pair costs 2 d flops per bf16 term
-    of the exact 3-term split of K-bar."""
+    of the 2-term split of K-bar."""
     esz = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
     pooled = int(sizes.pooled_rows)
     kv_bytes = 2 * w.total_tokens * w.hkv * w.d * esz
@@ -204,7 +204,7 @@ def stage_bytes_flops(w, sizes) -> dict:
             pairs += w.hkv * w.g * nq * (I + 1)
     scores = {"bytes": w.total_queries * w.hq * w.d * esz + pooled * w.hkv * w.d * 4 +
               int(sizes.score_elems) * 4,
-              "mfma_flops": 3 * 2 * w.d * pairs if w.dtype != "f32" else 0}
+              "mfma_flops": 2 * 2 * w.d * pairs if w.dtype != "f32" else 0}
     return {"pool": pool, "scores": scores}
 
 
@@ -238,7 +238,8 @@ def measure(bslp, torch, w, inp, steps: int, warmup: int, kv_splits: int, evict_
         rec(1)
         bslp.score_blocks(prob, q, bufs.kbar, bufs.scores, sp)
         rec(2)
-        bslp.select_blocks(prob, params, bufs.scores, bufs.counts, bufs.cu, bufs.idx, sp)
+        bslp.select_blocks(prob, params, q, bufs.kbar, bufs.scores, bufs.counts, bufs.cu, bufs.idx,
+                           sp)
         rec(3)
         bslp.sparse_prefill_attn(prob, params, q, k, v, bufs.kbar, bufs.vbar, bufs.cu, bufs.idx,
                                  bufs.out, bufs.lse, bufs.workspace, sp)
@@ -299,7 +300,7 @@ def summarize(w, m, peak_attn: float) -> dict:
             "pool_kv": {"bound": "hbm", "bytes": work["pool"]["bytes"], "ms": pool_ms,
                         "gbs": pool_gbs, "frac": pool_gbs / PEAK_HBM_GBS},
             "block_scores": {"bound": "mfma" if t_mfma > t_hbm else "hbm",
-                             "bytes": sc["bytes"], "mfma_flops_3term": sc["mfma_flops"],
+                             "bytes": sc["bytes"], "mfma_flops_2term": sc["mfma_flops"],
                              "ms": scores_ms, "gbs": sc_gbs, "hbm_frac": sc_gbs / PEAK_HBM_GBS,
                              "mfma_tflops": sc_tf,
                              "mfma_frac": sc_tf / PEAK_TFLOPS["bf16"],

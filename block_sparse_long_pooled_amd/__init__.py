@@ -101,7 +101,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bslp_block_scores.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, vp]
     lib.bslp_pool_kv.argtypes = [P(Problem), vp, vp, vp, vp, vp]
     lib.bslp_score_blocks.argtypes = [P(Problem), vp, vp, vp, vp]
-    lib.bslp_select_blocks.argtypes = [P(Problem), P(SelectParams), vp, vp, vp, vp, vp]
+    lib.bslp_select_blocks.argtypes = [P(Problem), P(SelectParams), vp, vp, vp, vp, vp, vp, vp]
     lib.bslp_sparse_prefill_attn.argtypes = [P(Problem), P(SelectParams), vp, vp, vp, vp, vp,
                                              vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.bslp_sparse_prefill_attn_noalloc.argtypes = [P(Problem), P(SelectParams), vp, vp, vp,
@@ -205,10 +205,12 @@ def score_blocks(problem, q, kbar, scores, stream=None):
                                             _ptr(scores), _stream(stream)))
 
 
-def select_blocks(problem, params, scores, counts, cu, idx, stream=None):
+def select_blocks(problem, params, q, kbar, scores, counts, cu, idx, stream=None):
+    """Selection from the score rows; q and kbar serve the exact re-decision
+    of blocks near the threshold."""
     _check(load_library().bslp_select_blocks(ctypes.byref(problem), ctypes.byref(params),
-                                             _ptr(scores), _ptr(counts), _ptr(cu), _ptr(idx),
-                                             _stream(stream)))
+                                             _ptr(q), _ptr(kbar), _ptr(scores), _ptr(counts),
+                                             _ptr(cu), _ptr(idx), _stream(stream)))
 
 
 def sparse_prefill_attn(problem, params, q, k, v, kbar, vbar, cu, idx, out, lse=None,
@@ -274,7 +276,8 @@ def prefill(problem, params, q, k, v, bufs: Buffers | None = None, stream=None) 
     """The three stages back to back on one stream."""
     bufs = bufs or Buffers(problem, q.device)
     block_scores(problem, q, k, v, bufs.kbar, bufs.vbar, bufs.scores, stream)
-    select_blocks(problem, params, bufs.scores, bufs.counts, bufs.cu, bufs.idx, stream)
+    select_blocks(problem, params, q, bufs.kbar, bufs.scores, bufs.counts, bufs.cu, bufs.idx,
+                  stream)
     sparse_prefill_attn(problem, params, q, k, v, bufs.kbar, bufs.vbar, bufs.cu, bufs.idx,
                         bufs.out, bufs.lse, bufs.workspace, stream)
     return bufs

@@ -283,8 +283,8 @@ bslp_status bslp_score_blocks(const bslp_problem* problem, const void* q, const 
 }
 
 bslp_status bslp_select_blocks(const bslp_problem* problem, const bslp_select_params* params,
-                               const float* scores, int32_t* counts, int32_t* cu, int32_t* idx,
-                               void* stream) {
+                               const void* q, const float* kbar, float* scores,
+                               int32_t* counts, int32_t* cu, int32_t* idx, void* stream) {
   bslp::Plan plan;
   bslp::KVDesc kv;
   bslp::SelectArgs a;
@@ -293,9 +293,11 @@ bslp_status bslp_select_blocks(const bslp_problem* problem, const bslp_select_pa
   st = check_params(params, &a);
   if (st != BSLP_OK) return st;
   if (!cu) return fail(BSLP_ERR_INVALID_ARG, "cu is NULL");
-  if (plan.num_segments > 0 && (!scores || !counts || !idx))
+  if (plan.num_segments > 0 && (!q || !kbar || !scores || !counts || !idx))
     return fail(BSLP_ERR_INVALID_ARG, "a tensor pointer is NULL");
-  return hip_result(bslp::launch_select(plan, a, scores, counts, cu, idx, (hipStream_t)stream),
+  return hip_result(bslp::launch_select(plan, a, q, kbar, problem->dtype,
+                                        problem->softmax_scale * host_scale(problem, 0), scores,
+                                        counts, cu, idx, (hipStream_t)stream),
                     "bslp_select_blocks");
 }
 

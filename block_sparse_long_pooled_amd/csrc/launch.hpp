@@ -39,8 +39,13 @@ bool scores_mfma_supported(const Plan& p, int dtype);
 hipError_t launch_scores_mfma(const Plan& p, int dtype, const void* q, const float* kbar,
                               float c2, float* scores, hipStream_t st);
 
-hipError_t launch_select(const Plan& p, const SelectArgs& a, const float* scores, int32_t* counts,
-                         int32_t* cu, int32_t* idx, hipStream_t st);
+// Selection; q, kbar and lscale = softmax_scale * q_scale serve the exact
+// float64 re-decision of blocks near the threshold.  The scores of the
+// re-decided blocks that are dropped are negated by the first pass and
+// restored by the last.
+hipError_t launch_select(const Plan& p, const SelectArgs& a, const void* q, const float* kbar,
+                         int dtype, float lscale, float* scores, int32_t* counts, int32_t* cu,
+                         int32_t* idx, hipStream_t st);
 
 hipError_t launch_attn_valu(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
                             hipStream_t st);

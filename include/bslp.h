@@ -162,10 +162,11 @@ bslp_status bslp_get_sizes(const bslp_problem* problem, bslp_sizes* out);
  *   Score_IJ = S'_IJ / sum_{K<=I} S'_IK, written to scores (float32 rows as
  *   described above).  Accuracy: float32 inputs accumulate the logits in
  *   float64 on the vector ALUs.  bf16 / fp8 inputs run on the matrix cores:
- *   q is exact in bf16 and kbar is split exactly into three bf16 terms, so
- *   every product is exact and only the float32 accumulation rounds; the
- *   scores carry a relative error of order 1e-5 (measured below 1e-5 on the
- *   64K and 128K workloads).
+ *   q is exact in bf16 and kbar is split into two bf16 terms (to within
+ *   2^-18 of itself), products are exact and the accumulation is float32;
+ *   the scores carry a relative error below 1e-3 (of order 1e-5 on the 64K
+ *   and 128K workloads), which bslp_select_blocks absorbs by deciding the
+ *   blocks near the threshold exactly.
  *
  * q: [T, Hq, d] in the problem dtype.  k, v: [T, Hkv, d], or physical rows
  * [*, Hkv, d] through the page table.  All device pointers. */
@@ -193,10 +194,22 @@ bslp_status bslp_score_blocks(const bslp_problem* problem, const void* q, const 
  *   cu[s]     = sum_{s'<s} counts[s'], cu[num_segments] = total
  *                                                         [num_segments + 1]
  *   idx[cu[s] .. cu[s+1]) = Sel of segment s, ascending  [score_elems capacity]
- * alpha = 0 selects every causal block (dense attention). */
+ * alpha = 0 selects every causal block (dense attention).
+ * Exactness: the scores carry a relative error below 1e-3; every block
+ * whose score lies within 2e-3 (relative) of thresh_I is re-decided exactly
+ * in float64 from q and kbar (the comparison E_J >= alpha max_K E_K of block
+ * energies E_J = sum_r exp(s_rJ - m), the maximum taken over the blocks
+ * within 2e-3 of the largest score), so the selection is the definition's
+ * outside a float64-rounding band.  q and kbar are the inputs of stage 1
+ * for the same problem (kbar from bslp_block_scores / bslp_pool_kv).
+ * scores: read, and borrowed in between: the call's first pass hands the
+ * exact decisions to its last pass by negating the scores of the re-decided
+ * blocks it drops, and the last pass restores them, so when the call's work
+ * on `stream` has completed the buffer holds bitwise what it held before.
+ * No other work may read or write scores while the call's work runs. */
 bslp_status bslp_select_blocks(const bslp_problem* problem, const bslp_select_params* params,
-                               const float* scores, int32_t* counts, int32_t* cu, int32_t* idx,
-                               void* stream);
+                               const void* q, const float* kbar, float* scores,
+                               int32_t* counts, int32_t* cu, int32_t* idx, void* stream);
 
 /* Stage 3: block-sparse causal attention with mean correction
  * (FlashPrefill V2, Sec. 3.1 last sentence, Sec. 3.2 and Fig. 3, PackGQA and

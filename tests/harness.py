@@ -496,7 +496,9 @@ def compare_selection(w: Workload, g: GpuResult, rows: dict, alpha=None) -> Repo
 def assert_parity(w: Workload, rep: Report):
     assert rep.tiles > 0
     assert rep.sel_mismatch == 0, str(rep)
-    assert rep.score_rel < 1e-4, str(rep)
+    # the selection re-decides blocks within 2 x 1e-3 of the threshold exactly,
+    # which assumes score errors below 1e-3; half of it leaves a margin
+    assert rep.score_rel < 5e-4, str(rep)
     assert rep.kbar_err < 1e-4, str(rep)
     assert rep.out_err <= out_tol(w.dtype), str(rep)
     assert rep.lse_err <= (1e-3 if w.dtype == "f32" else 2e-2), str(rep)

@@ -113,7 +113,7 @@ def test_params_validation(kw):
     if kw.get("correction") == 2:
         params.mean_correction = 2
     t = FakeTensor()
-    st, _ = _status(lambda: bslp.select_blocks(_problem(), params, t, t, t, t, stream=0))
+    st, _ = _status(lambda: bslp.select_blocks(_problem(), params, t, t, t, t, t, t, stream=0))
     assert st == 1
 
 
@@ -123,7 +123,9 @@ def test_null_pointers_rejected_before_launch():
     t = FakeTensor()
     st, d = _status(lambda: bslp.block_scores(p, t, t, None, t, t, t, stream=0))
     assert st == 1 and "NULL" in d
-    st, _ = _status(lambda: bslp.select_blocks(p, params, t, t, None, t, stream=0))
+    st, _ = _status(lambda: bslp.select_blocks(p, params, t, t, t, t, None, t, stream=0))
+    st2, _ = _status(lambda: bslp.select_blocks(p, params, None, t, t, t, t, t, stream=0))
+    assert st2 == 1
     assert st == 1
     st, _ = _status(lambda: bslp.sparse_prefill_attn(p, params, t, t, t, t, t, t, None, t,
                                                      stream=0))

@@ -164,6 +164,39 @@ def test_pool_and_score_halves_equal_block_scores():
             assert torch.equal(getattr(a, n), getattr(b, n)), (w.name, n)
 
 
+def test_select_leaves_scores_bitwise_unchanged():
+    # the selection's count pass negates the scores of the uncertain blocks it
+    # drops after the exact re-decision, and the emit pass restores them; the
+    # 64K workload has hundreds of segments with a score in the uncertain
+    # band (2e-3 relative around alpha times the row maximum), so the path runs
+    import torch
+
+    import block_sparse_long_pooled_amd as bslp
+    w = SWEEP_BF16_64K
+    inp = make_inputs(w, 0)
+    q, k, v, _ = to_device(inp)
+    prob = bslp.make_problem(w.dtype, w.hq, w.hkv, w.d, w.block, w.seqlens, softmax_scale=w.scale)
+    params = bslp.make_params(w.alpha, w.sink, w.window, w.recent, w.correction)
+    bufs = bslp.Buffers(prob)
+    bslp.pool_kv(prob, k, v, bufs.kbar, bufs.vbar)
+    bslp.score_blocks(prob, q, bufs.kbar, bufs.scores)
+    before = bufs.scores.clone()
+    for _ in range(2):
+        bslp.select_blocks(prob, params, q, bufs.kbar, bufs.scores, bufs.counts, bufs.cu, bufs.idx)
+    torch.cuda.synchronize()
+    assert torch.equal(before.view(torch.int32), bufs.scores.view(torch.int32))
+    sc = before.cpu().numpy()
+    banded = 0
+    for (b, h, I, s, off) in segments(w.seqlens, w.hkv, w.block):
+        row = sc[off:off + I + 1]
+        th = np.float32(w.alpha) * row.max()
+        J = np.arange(I + 1)
+        free = (J >= w.sink) & (J < I - w.recent - w.window + 1)
+        banded += int(((row >= th * np.float32(0.998)) & (row <= th * np.float32(1.002)) & free).any())
+    log(f"[select] segments with a score in the uncertain band: {banded}")
+    assert banded > 0
+
+
 def test_deterministic_bitwise():
     w = GQA_BF16_16K.replace(seqlens=(4096,))
     inp = make_inputs(w, 0)
@@ -214,7 +247,7 @@ def _full_size(w, seed, rows=None, whole_head=None, per_head=3, dev=None, inp=No
     log(f"[parity] {w.name} every segment: {sel}")
     assert sel.tiles == len(segments(w.seqlens, w.hkv, w.block, w.query_lens))
     assert sel.sel_mismatch == 0, str(sel)
-    assert sel.score_rel < 1e-4, str(sel)
+    assert sel.score_rel < 5e-4, str(sel)
     tiles = sample_tiles(w, per_head=per_head, seed=seed)
     if whole_head is not None:
         for b, (L, Lq) in enumerate(zip(w.seqlens, w.query_lens)):

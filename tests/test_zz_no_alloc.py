@@ -34,7 +34,7 @@ def _both(w, seed, kv_splits=0):
     params = bslp.make_params(w.alpha, w.sink, w.window, w.recent, w.correction)
     bufs = bslp.Buffers(prob)
     bslp.block_scores(prob, q, k, v, bufs.kbar, bufs.vbar, bufs.scores)
-    bslp.select_blocks(prob, params, bufs.scores, bufs.counts, bufs.cu, bufs.idx)
+    bslp.select_blocks(prob, params, q, bufs.kbar, bufs.scores, bufs.counts, bufs.cu, bufs.idx)
     bslp.sparse_prefill_attn(prob, params, q, k, v, bufs.kbar, bufs.vbar, bufs.cu, bufs.idx,
                              bufs.out, bufs.lse, bufs.workspace)
     out2 = torch.full_like(bufs.out, float("nan"))
