@@ -212,19 +212,23 @@ def percentile(x, q):
     return float(np.percentile(np.asarray(x, dtype=np.float64), q))
 
 
-def measure(bslp, torch, w, inp, steps: int, warmup: int, kv_splits: int, evict_bytes: int):
+def measure(bslp, torch, w, inp, steps: int, warmup: int, kv_splits: int, evict_bytes: int,
+            v_dmajor: bool = False):
     """Runs the layer `warmup + steps` times with HIP events around each
     kernel launch on the launch stream; between steps a scratch buffer of
     evict_bytes is written so the next step starts with cold caches (MALL and
     L2).  Returns per-step stage times (ms) and the buffers of the last step."""
     dev = torch.device("cuda")
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    if v_dmajor:  # [Hkv, d, kv tokens] (contiguous K/V only here)
+        v = v.permute(1, 2, 0).contiguous()
     table = torch.from_numpy(inp.table).to(dev) if inp.table is not None else None
     prob = bslp.make_problem(w.dtype, w.hq, w.hkv, w.d, w.block, w.query_lens,
                              softmax_scale=w.scale, q_scale=inp.q_scale, k_scale=inp.k_scale,
                              v_scale=inp.v_scale, page_table=table, page_size=w.page_size,
                              kv_splits=kv_splits,
-                             kv_seqlens=w.seqlens if w.q_lens is not None else None)
+                             kv_seqlens=w.seqlens if w.q_lens is not None else None,
+                             v_dmajor=v_dmajor)
     params = bslp.make_params(w.alpha, w.sink, w.window, w.recent, w.correction)
     bufs = bslp.Buffers(prob)
     stream = torch.cuda.current_stream()
@@ -326,6 +330,8 @@ def main():
                     help="timed online e4m3 quantisations of Q for bf16 workloads (0 skips)")
     ap.add_argument("--dense-reps", type=int, default=3,
                     help="timed calls of the dense causal path (0 skips it)")
+    ap.add_argument("--v-dmajor-ab", action="store_true",
+                    help="also time the 128K fp8 workload with V given d-major")
     ap.add_argument("--fp8-steps", type=int, default=8,
                     help="timed steps of the 128K fp8 workload reported beside the default "
                          "64K bf16 one (0 skips it)")
@@ -458,6 +464,16 @@ def main():
             "note": "P V on the fp8 matrix cores (e4m3 probabilities), Q K^T on the bf16 "
                     "matrix cores on exactly widened codes; frac against the 5 PF fp8 peak",
         }
+        if args.v_dmajor_ab:
+            # the same workload with V given d-major ([Hkv, d, kv tokens])
+            del m8
+            torch.cuda.empty_cache()
+            md = measure(bslp, torch, w8, inp8, args.fp8_steps, 2, args.kv_splits, evict,
+                         v_dmajor=True)
+            sd = summarize(w8, md, PEAK_TFLOPS["fp8"])
+            res["fp8_128k"]["v_dmajor"] = {"ms_per_layer": sd["layer_ms"]["median"],
+                                           "stages_ms": sd["stages_ms"],
+                                           "attention": sd["attention"]}
     print(json.dumps(res), flush=True)
 
 

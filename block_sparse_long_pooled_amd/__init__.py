@@ -52,6 +52,7 @@ class Problem(ctypes.Structure):
         ("kv_splits", ctypes.c_int32),
         ("scales_dev", ctypes.c_void_p),
         ("kv_seqlens", ctypes.POINTER(ctypes.c_int32)),
+        ("v_layout", ctypes.c_int32),
     ]
 
 
@@ -129,14 +130,16 @@ def _check(status: int):
 def make_problem(dtype: str, hq: int, hkv: int, head_dim: int, block_size: int, seqlens,
                  softmax_scale: float | None = None, q_scale: float = 1.0, k_scale: float = 1.0,
                  v_scale: float = 1.0, page_table=None, page_size: int = 0,
-                 kv_splits: int = 0, scales_dev=None, kv_seqlens=None) -> Problem:
+                 kv_splits: int = 0, scales_dev=None, kv_seqlens=None,
+                 v_dmajor: bool = False) -> Problem:
     """Fills the problem descriptor.  `page_table` is a device int32 tensor
     [num_seqs, max_pages] (or None for contiguous K/V); `kv_splits` 0 lets the
     library choose the attention's KV splits, 1 turns them off; `scales_dev`
     (fp8) is a device float32 tensor of (q, k, v) scales that replaces the
     host scales, e.g. filled by quantize_e4m3.  `kv_seqlens` gives each
     request's key count when its queries are only the last `seqlens[b]`
-    positions (a chunk of a chunked prefill)."""
+    positions (a chunk of a chunked prefill).  `v_dmajor` (fp8): V is given
+    as [Hkv, d, kv tokens] (or [pages, Hkv, d, page_size] when paged)."""
     lens = (ctypes.c_int32 * len(seqlens))(*[int(x) for x in seqlens])
     p = Problem()
     p.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
@@ -146,6 +149,7 @@ def make_problem(dtype: str, hq: int, hkv: int, head_dim: int, block_size: int, 
     p.q_scale, p.k_scale, p.v_scale = q_scale, k_scale, v_scale
     p.num_seqs = len(seqlens)
     p.kv_splits = kv_splits
+    p.v_layout = 1 if v_dmajor else 0
     if scales_dev is not None:
         p.scales_dev = scales_dev.data_ptr()
     p.seqlens = lens

@@ -66,12 +66,19 @@ bslp_status build_plan(const bslp_problem* pr, bslp::Plan* plan, bslp::KVDesc* k
     return fail(BSLP_ERR_INVALID_ARG, "scales_dev is for fp8 inputs only");
   if (reinterpret_cast<uintptr_t>(pr->scales_dev) % 4)
     return fail(BSLP_ERR_INVALID_ARG, "scales_dev must be 4-byte aligned");
+  if (pr->v_layout != BSLP_V_ROWS && pr->v_layout != BSLP_V_DMAJOR)
+    return fail(BSLP_ERR_INVALID_ARG, "v_layout must be BSLP_V_ROWS or BSLP_V_DMAJOR");
+  if (pr->v_layout == BSLP_V_DMAJOR && pr->dtype != BSLP_FP8_E4M3)
+    return fail(BSLP_ERR_UNSUPPORTED, "d-major V is built for fp8 inputs only");
+  if (pr->v_layout == BSLP_V_DMAJOR && pr->page_table && pr->page_size < 64)
+    return fail(BSLP_ERR_UNSUPPORTED, "d-major V needs pages of at least 64 tokens");
 
   *plan = bslp::Plan{};
   plan->num_seqs = pr->num_seqs;
   plan->hq = pr->num_heads_q;
   plan->hkv = pr->num_heads_kv;
   plan->dscale = pr->scales_dev;
+  plan->v_dmajor = pr->v_layout == BSLP_V_DMAJOR;
   plan->g = g;
   plan->d = pr->head_dim;
   plan->B = pr->block_size;
@@ -109,6 +116,8 @@ bslp_status build_plan(const bslp_problem* pr, bslp::Plan* plan, bslp::KVDesc* k
     if (kvtok >= (int64_t(1) << 31) || score >= (int64_t(1) << 31))
       return fail(BSLP_ERR_UNSUPPORTED, "problem exceeds 2^31 tokens or index entries");
   }
+  if (plan->v_dmajor && !pr->page_table && (int64_t)plan->d * kvtok >= (int64_t(1) << 31))
+    return fail(BSLP_ERR_UNSUPPORTED, "d-major V beyond 2^31 bytes needs paged K/V");
   plan->max_nblk = max_nblk;
   // heaviest requests first (stable insertion sort, at most 64 entries)
   for (int i = 0; i < pr->num_seqs; ++i) {
@@ -156,7 +165,7 @@ bslp_status hip_result(hipError_t e, const char* what) {
 hipError_t launch_attn(const bslp::Plan& plan, const bslp::KVDesc& kv, int dtype,
                        const bslp::AttnArgs& a, hipStream_t stream) {
   if (dtype == BSLP_F32) return bslp::launch_attn_valu(plan, kv, dtype, a, stream);
-  if (dtype == BSLP_FP8_E4M3) return bslp::launch_attn_fp8(plan, kv, a, 0, stream);
+  if (dtype == BSLP_FP8_E4M3) return bslp::launch_attn_fp8(plan, kv, a, stream);
   return bslp::launch_attn_mfma(plan, kv, dtype, a, stream);
 }
 

@@ -79,7 +79,9 @@ struct F8Cfg {
 template <int D, int NW>
 struct F8Prefetch {
   uint2 k[F8Cfg<D, NW>::KL];    // 8 e4m3 codes of one key
-  u32x4_t v[F8Cfg<D, NW>::PL];  // row-major: 4 keys' 4 bytes; column-major: 16 key bytes
+  u32x4_t v[F8Cfg<D, NW>::PL];  // row-major: 4 keys' 4 bytes; d-major: 20 bytes from a
+  uint32_t vx[F8Cfg<D, NW>::PL];  //   4-byte boundary (v, vx) holding 16 keys at byte vs
+  uint32_t vs[F8Cfg<D, NW>::PL];
 };
 
 // Global -> registers for one step.  Exact steps read tokens key0.. of the
@@ -123,7 +125,13 @@ __device__ __forceinline__ void f8_fetch(F8Prefetch<D, NW>& pf, const Step& st, 
       pf.k[i] = make_uint2(w[0], w[1]);
     }
     if (VCOL && exact) {
-      // V^T rows of d: [Hkv, d, kv tokens], or [pages, Hkv, d, page]
+      // V^T rows of d: [Hkv, d, kv tokens], or [pages, Hkv, d, page].  The
+      // token stride need not be a multiple of 4, and the buffer range is
+      // checked a 4-byte word at a time, so the loads start from the 4-byte
+      // boundary below key0 (sh0 bytes before it) and each 16-key piece is
+      // read as 20 bytes from the boundary below it, realigned when stored.
+      // The range ends at the word holding the last valid key of row D-1,
+      // inside the V array (whose end is a 4-byte boundary).
       int64_t base;
       int64_t dstride;
       if (paged) {
@@ -133,14 +141,17 @@ __device__ __forceinline__ void f8_fetch(F8Prefetch<D, NW>& pf, const Step& st, 
         dstride = kv_tokens;
         base = (int64_t)u.h * D * dstride + row0;
       }
+      const int sh0 = (int)(base & 3);
+      const int span = sh0 + (int)((D - 1) * dstride) + last + 1;
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)uniform_ptr(v + base), (short)0, uni((int)((D - 1) * dstride + last + 1)),
-          kRsrcWord3);
+          (void*)uniform_ptr(v + (base - sh0)), (short)0, uni((span + 3) & ~3), kRsrcWord3);
 #pragma unroll
       for (int i = 0; i < C::PL; ++i) {
         const int f = min(tid + i * C::NT, C::NP - 1);
-        pf.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)((f >> 2) * dstride + (f & 3) * 16),
-                                                        0, 0);
+        const int pos = sh0 + (int)((f >> 2) * dstride) + (f & 3) * 16;
+        pf.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, pos & ~3, 0, 0);
+        pf.vx[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, (pos & ~3) + 16, 0, 0);
+        pf.vs[i] = (uint32_t)(pos & 3);
       }
     } else {
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -180,6 +191,13 @@ __device__ __forceinline__ void f8_fetch(F8Prefetch<D, NW>& pf, const Step& st, 
   }
 }
 
+// Last valid key (0 .. 63) of an exact step: keys past the request end are
+// masked; 63 for every other step.
+__device__ __forceinline__ int step_last_key(const Step& st, const UnitCtx& u) {
+  if (st.kind != kExact) return kKeys - 1;
+  return min(kKeys, u.len - (st.J * u.B + st.hf * kKeys)) - 1;
+}
+
 // Eight e4m3 codes widened to eight bf16, exactly (an e4m3 value has 4
 // significant bits; its float32 bits end in 16 zeros).
 __device__ __forceinline__ u32x4_t widen8(uint2 w) {
@@ -197,8 +215,8 @@ __device__ __forceinline__ u32x4_t widen8(uint2 w) {
 // Registers -> LDS: K rows widened to bf16 at their permuted rows, V^T
 // [d][keys] (swizzled 16-byte chunks), transposed here from row-major pieces.
 template <int D, int NW>
-__device__ __forceinline__ void f8_store(const F8Prefetch<D, NW>& pf, bool vcol, uint8_t* Ks,
-                                         uint8_t* Vt) {
+__device__ __forceinline__ void f8_store(const F8Prefetch<D, NW>& pf, bool vcol, int vlast,
+                                         uint8_t* Ks, uint8_t* Vt) {
   using C = F8Cfg<D, NW>;
   const int tid = threadIdx.x;
 #pragma unroll
@@ -214,7 +232,22 @@ __device__ __forceinline__ void f8_store(const F8Prefetch<D, NW>& pf, bool vcol,
       const int f = tid + i * C::NT;
       if (C::NP % C::NT != 0 && f >= C::NP) break;
       const int d = f >> 2, ch = f & 3;
-      *reinterpret_cast<u32x4_t*>(Vt + d * C::VROW + ((ch ^ vswz(d)) << 4)) = pf.v[i];
+      const u32x4_t r = pf.v[i];
+      const uint32_t sb = pf.vs[i];  // the piece starts sb bytes into the 20 loaded
+      u32x4_t x = {__builtin_amdgcn_alignbyte(r[1], r[0], sb),
+                   __builtin_amdgcn_alignbyte(r[2], r[1], sb),
+                   __builtin_amdgcn_alignbyte(r[3], r[2], sb),
+                   __builtin_amdgcn_alignbyte(pf.vx[i], r[3], sb)};
+      // keys past the request's last one hold other tokens (or unwritten page
+      // bytes, possibly the NaN code): zero, so that 0 x V stays 0
+      if (ch * 16 + 15 > vlast) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int keep = vlast - (ch * 16 + 4 * w) + 1;  // bytes of this word to keep
+          x[w] &= keep <= 0 ? 0u : keep >= 4 ? ~0u : (1u << (8 * keep)) - 1u;
+        }
+      }
+      *reinterpret_cast<u32x4_t*>(Vt + d * C::VROW + ((ch ^ vswz(d)) << 4)) = x;
     }
     return;
   }
@@ -430,7 +463,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fp8_kernel(
   Step cur = first_step(u, idx, selbits, correction);
   if (cur.kind != kDone) {
     f8_fetch<D, NW, VCOL>(pf, cur, u, kv, p.hkv, p.kv_tokens, k, v, kq, vq);
-    f8_store<D, NW>(pf, VCOL && cur.kind == kExact, Ks[0], Vt[0]);
+    f8_store<D, NW>(pf, VCOL && cur.kind == kExact, step_last_key(cur, u), Ks[0], Vt[0]);
   }
   uniform(cur);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): query rows and the first step
@@ -449,7 +482,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fp8_kernel(
       advance(nn, u, idx, selbits, correction);
       uniform(nn);
     }
-    if (nxt.kind != kDone) f8_store<D, NW>(pf, VCOL && nxt.kind == kExact, Ks[buf ^ 1], Vt[buf ^ 1]);
+    if (nxt.kind != kDone)
+      f8_store<D, NW>(pf, VCOL && nxt.kind == kExact, step_last_key(nxt, u), Ks[buf ^ 1],
+                      Vt[buf ^ 1]);
     if (nn.kind != kDone) f8_fetch<D, NW, VCOL>(pf, nn, u, kv, p.hkv, p.kv_tokens, k, v, kq, vq);
     if (wave_active) {
       int mode, key0 = 0;
@@ -563,6 +598,17 @@ __device__ __forceinline__ uint32_t e4m3_of_ratio(int64_t num, int sh) {
   return sign | code;
 }
 
+// e4m3 code of the mean of a block's cnt codes, from their exact integer sum
+// acc = sum code x 2^9: a power-of-two count scales exactly; any other count
+// (a short last block, never corrected) is rounded once, from float64.
+__device__ __forceinline__ uint32_t pooled_code(int acc, int cnt) {
+  int sh = 9;  // code x 2^9 is an integer; the mean divides by cnt
+  while ((1 << (sh - 9)) < cnt) ++sh;
+  if ((1 << (sh - 9)) == cnt) return e4m3_of_ratio(acc, sh);
+  const double m = (double)acc / (512.0 * cnt);
+  return e4m3_of_ratio((int64_t)rint(ldexp(m, 20)), 20);
+}
+
 // Pooled statistics of the fp8 correction steps, quantised as in FP8 mode:
 // kq = e4m3(mean of the block's K codes), vq likewise for V, both [pooled
 // row, Hkv, d] bytes.  The codes of a block are summed exactly as integers
@@ -570,7 +616,8 @@ __device__ __forceinline__ uint32_t e4m3_of_ratio(int64_t num, int sh) {
 // on the exact mean - block means of e4m3 codes often sit exactly on an
 // e4m3 midpoint, where a float32 round trip through kbar / c_k would break
 // the tie either way.  One workgroup per (pooled row, K or V); each thread
-// sums 8 columns over the block's rows.
+// sums 8 columns over the block's rows.  A d-major V takes
+// pool_v_dmajor_kernel instead (the grid then covers K only).
 __global__ __launch_bounds__(256) void pooled_e4m3_kernel(Plan p, KVDesc kv,
                                                           const uint8_t* __restrict__ k,
                                                           const uint8_t* __restrict__ v,
@@ -583,9 +630,6 @@ __global__ __launch_bounds__(256) void pooled_e4m3_kernel(Plan p, KVDesc kv,
   const SeqInfo s = p.seq[b];
   const int j0 = (prow - s.pool_base) * p.B;
   const int cnt = min(p.B, s.len - j0);
-  int sh = 9;  // code x 2^9 is an integer; the mean divides by cnt
-  while ((1 << (sh - 9)) < cnt) ++sh;
-  const bool pow2 = (1 << (sh - 9)) == cnt;
   const uint8_t* x = is_v ? v : k;
   uint8_t* out = (is_v ? vq : kq) + (int64_t)prow * p.hkv * p.d;
   const int ncol8 = p.hkv * p.d / 8;
@@ -605,15 +649,7 @@ __global__ __launch_bounds__(256) void pooled_e4m3_kernel(Plan p, KVDesc kv,
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      // mean = acc / (cnt 2^9): a power-of-two count scales exactly; any
-      // other count (a short last block, never corrected) is rounded once
-      uint32_t c;
-      if (pow2) {
-        c = e4m3_of_ratio(acc[e], sh);
-      } else {
-        const double m = (double)acc[e] / (512.0 * cnt);
-        c = e4m3_of_ratio((int64_t)rint(ldexp(m, 20)), 20);
-      }
+      const uint32_t c = pooled_code(acc[e], cnt);
       if (e < 4)
         lo |= c << (8 * e);
       else
@@ -621,6 +657,83 @@ __global__ __launch_bounds__(256) void pooled_e4m3_kernel(Plan p, KVDesc kv,
     }
     *reinterpret_cast<uint2*>(out + c8 * 8) = make_uint2(lo, hi);
   }
+}
+
+// Pooled means of a d-major fp8 V ([Hkv, d, kv tokens], or [pages, Hkv, d,
+// page] with pages of at least 64 tokens).  Eight lanes per (pooled row,
+// head, dim): lane e reads tokens 16e .. 16e + 15 of the block (one 16-byte
+// piece, inside one page), the codes are summed exactly as integers (code x
+// 2^9 is an integer) and the eight lanes' sums are added.  With vq the e4m3
+// code of each mean is written (the quantised pooled values of the fp8
+// correction), else vbar = the float32 mean times the V scale, formed as the
+// row-major pooling forms it (sum / count * scale).
+__global__ __launch_bounds__(256) void pool_v_dmajor_kernel(Plan p, KVDesc kv,
+                                                            const uint8_t* __restrict__ v,
+                                                            float v_scale,
+                                                            float* __restrict__ vbar,
+                                                            uint8_t* __restrict__ vq) {
+  const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
+  const int e = threadIdx.x & 7;
+  const int hd_n = p.hkv * p.d;
+  const bool in = item < (int64_t)p.pooled_rows * hd_n;  // every lane stays for the shuffles
+  int acc = 0, cnt = 1;
+  int64_t o = 0;
+  if (in) {
+    const int prow = (int)(item / hd_n);
+    const int hd = (int)(item % hd_n);  // h * d + dim
+    o = item;
+    int b = 0;
+    while (b + 1 < p.num_seqs && p.seq[b + 1].pool_base <= prow) ++b;
+    const SeqInfo s = p.seq[b];
+    const int j0 = (prow - s.pool_base) * p.B;
+    cnt = min(p.B, s.len - j0);
+    const int r0 = 16 * e;
+    if (r0 < cnt) {
+      const int j = j0 + r0;
+      int64_t off;
+      if (kv.page_table != nullptr) {
+        const int64_t phys = kv.page_table[(int64_t)b * kv.max_pages + (j >> kv.page_shift)];
+        off = ((phys * hd_n + hd) << kv.page_shift) + (j & ((1 << kv.page_shift) - 1));
+      } else {
+        off = (int64_t)hd * p.kv_tokens + s.kv_start + j;
+      }
+      const int m = min(16, cnt - r0);
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (m == 16 && (off & 15) == 0) {
+        const uint4 u = *reinterpret_cast<const uint4*>(v + off);
+        w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+      } else {
+        for (int t = 0; t < m; ++t) w[t >> 2] |= (uint32_t)v[off + t] << (8 * (t & 3));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+        const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+        acc += (int)(f0[0] * 512.f) + (int)(f0[1] * 512.f) + (int)(f1[0] * 512.f) +
+               (int)(f1[1] * 512.f);  // exact; a zero code adds nothing
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (!in || e != 0) return;
+  if (vq) {
+    vq[o] = (uint8_t)pooled_code(acc, cnt);
+  } else {
+    const float sc = p.dscale ? p.dscale[2] : v_scale;
+    const float t = (float)acc * (1.f / 512.f);
+    vbar[o] = t / (float)cnt * sc;
+  }
+}
+
+hipError_t launch_pool_v_dmajor(const Plan& p, const KVDesc& kv, const void* v, float v_scale,
+                                float* vbar, uint8_t* vq, hipStream_t st) {
+  const int64_t lanes = (int64_t)p.pooled_rows * p.hkv * p.d * 8;
+  if (lanes == 0) return hipSuccess;
+  hipLaunchKernelGGL(pool_v_dmajor_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st,
+                     p, kv, static_cast<const uint8_t*>(v), v_scale, vbar, vq);
+  return hipGetLastError();
 }
 
 namespace {
@@ -642,11 +755,15 @@ hipError_t launch_fp8_t(const Plan& p, const KVDesc& kv, const AttnArgs& a, hipS
   uint8_t* vq = kq + n;
   const int corr = a.correction && !a.dense;
   if (n > 0 && corr) {
-    hipLaunchKernelGGL(pooled_e4m3_kernel, dim3((unsigned)p.pooled_rows, 2), dim3(256), 0, st, p,
-                       kv, static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), kq,
-                       vq);
-    const hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL(pooled_e4m3_kernel, dim3((unsigned)p.pooled_rows, VCOL ? 1 : 2), dim3(256),
+                       0, st, p, kv, static_cast<const uint8_t*>(a.k),
+                       static_cast<const uint8_t*>(a.v), kq, vq);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (VCOL) {
+      e = launch_pool_v_dmajor(p, kv, a.v, a.v_scale, nullptr, vq, st);
+      if (e != hipSuccess) return e;
+    }
   }
   // logits of the codes: softmax_scale * q_scale * k_scale, in units of log2
   const float c = (float)((double)a.lscale * (double)a.k_scale * 1.4426950408889634);
@@ -696,9 +813,9 @@ hipError_t launch_fp8_d(const Plan& p, const KVDesc& kv, const AttnArgs& a, hipS
 
 }  // namespace
 
-hipError_t launch_attn_fp8(const Plan& p, const KVDesc& kv, const AttnArgs& a, int v_colmajor,
-                           hipStream_t st) {
-  if (v_colmajor) return hipErrorInvalidValue;
+hipError_t launch_attn_fp8(const Plan& p, const KVDesc& kv, const AttnArgs& a, hipStream_t st) {
+  if (p.v_dmajor)
+    return p.d == 128 ? launch_fp8_d<128, true>(p, kv, a, st) : launch_fp8_d<64, true>(p, kv, a, st);
   return p.d == 128 ? launch_fp8_d<128, false>(p, kv, a, st) : launch_fp8_d<64, false>(p, kv, a, st);
 }
 

@@ -64,6 +64,7 @@ struct Plan {
   int32_t order[kMaxSeqs];  // requests by descending block count (ties: packed order)
   // fp8 scales (q, k, v) in device memory, or nullptr: the host floats apply
   const float* dscale;
+  int32_t v_dmajor;  // V as [Hkv, d, kv tokens] (or [pages, Hkv, d, page]), fp8 only
 };
 
 // Where key/value token j of request b lives.

@@ -82,10 +82,14 @@ hipError_t launch_split_merge(const Plan& p, const int32_t* cu, const SplitBufs&
 hipError_t persistent_grid(const Plan& p, int splits, int per_cu, int64_t* grid);
 
 // fp8 inputs on the fp8 matrix cores (e4m3 probabilities, FlashPrefill V2 FP8
-// arithmetic); v_colmajor: V given as [Hkv, d, kv tokens] (contiguous) or
+// arithmetic); with p.v_dmajor, V is [Hkv, d, kv tokens] (contiguous) or
 // [pages, Hkv, d, page_size] (paged).
-hipError_t launch_attn_fp8(const Plan& p, const KVDesc& kv, const AttnArgs& a, int v_colmajor,
-                           hipStream_t st);
+hipError_t launch_attn_fp8(const Plan& p, const KVDesc& kv, const AttnArgs& a, hipStream_t st);
+
+// Pooled means of a d-major fp8 V: vbar (float32, times the V scale) or,
+// with codes, the e4m3 code of each mean (the quantised pooled values).
+hipError_t launch_pool_v_dmajor(const Plan& p, const KVDesc& kv, const void* v, float v_scale,
+                                float* vbar, uint8_t* vq, hipStream_t st);
 
 // Size of the device array that serves as the attention workspace of the
 // entry point that allocates nothing, and its address on the current device

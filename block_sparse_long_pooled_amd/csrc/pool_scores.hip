@@ -237,11 +237,17 @@ static hipError_t launch_stage1_t(const Plan& p, const KVDesc& kv, const void* q
   using T = typename Elem<DT>::T;
   if ((parts & kStagePool) && p.pooled_rows > 0) {
     const int groups = (p.hkv + pool_heads<D>() - 1) / pool_heads<D>();
-    dim3 grid((unsigned)p.pooled_rows, (unsigned)groups, 2);
+    // a d-major (fp8) V is pooled by its own kernel; the grid then covers K
+    const bool vrows = !(DT == kFP8 && p.v_dmajor);
+    dim3 grid((unsigned)p.pooled_rows, (unsigned)groups, vrows ? 2 : 1);
     hipLaunchKernelGGL((pool_kernel<DT, D>), grid, dim3(kPoolThreads), 0, st, p, kv, (const T*)k,
                        (const T*)v, k_scale, v_scale, kbar, vbar);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (!vrows) {
+      e = launch_pool_v_dmajor(p, kv, v, v_scale, vbar, nullptr, st);
+      if (e != hipSuccess) return e;
+    }
   }
   if (!(parts & kStageScores)) return hipSuccess;
   if (p.num_segments > 0 && scores_mfma_supported(p, DT)) {

@@ -120,7 +120,21 @@ typedef struct bslp_problem {
   /* HOST array [num_seqs]: keys L_b >= seqlens[b], N_b <= 16384; NULL means
    * L_b = seqlens[b] (self prefill of whole prompts). */
   const int32_t* kv_seqlens;
+  /* Layout of V (FlashPrefill V2, FP8 paragraph: the fp8 P~V product takes
+   * V with the keys along the contiguous dimension).
+   *   BSLP_V_ROWS (0): like K, [kv tokens, Hkv, d] (or [pages * page_size,
+   *     Hkv, d] when paged);
+   *   BSLP_V_DMAJOR (1), fp8 only: [Hkv, d, kv tokens] contiguous, or
+   *     [pages, Hkv, d, page_size] paged with page_size >= 64; token j of
+   *     request b is column kv_start_b + j (contiguous) or column j %
+   *     page_size of its page.  Every V reader (pooling, the quantised
+   *     pooled values, attention) takes this layout; outputs do not change.
+   * Anything else is BSLP_ERR_INVALID_ARG; d-major V with a non-fp8 dtype or
+   * pages below 64 tokens is BSLP_ERR_UNSUPPORTED. */
+  int32_t v_layout;
 } bslp_problem;
+
+enum { BSLP_V_ROWS = 0, BSLP_V_DMAJOR = 1 };
 
 /* Selection hyper-parameters (FlashPrefill V2, Sec. 3.1 and Sec. 4: alpha and
  * the sink/window sizes are user settings).  Counts are in blocks:

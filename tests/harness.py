@@ -64,8 +64,17 @@ def to_device(inp):
     return inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), table
 
 
+def v_dmajor(w: Workload, v):
+    """V in the d-major layout of the C ABI: [Hkv, d, kv tokens] from [tokens,
+    Hkv, d], or [pages, Hkv, d, page] from the paged [pages * page, Hkv, d]."""
+    if w.page_size:
+        p = w.page_size
+        return v.reshape(-1, p, w.hkv, w.d).permute(0, 2, 3, 1).contiguous()
+    return v.permute(1, 2, 0).contiguous()
+
+
 def run_gpu(w: Workload, inp, alpha=None, correction=None, dev_tensors=None,
-            kv_splits: int = 0, check: bool = True) -> GpuResult:
+            kv_splits: int = 0, check: bool = True, v_dmajor: bool = False) -> GpuResult:
     """One prefill through the C ABI on poisoned output buffers; with `check`
     the whole-array checks (check_arrays) run on the result."""
     import torch
@@ -76,7 +85,8 @@ def run_gpu(w: Workload, inp, alpha=None, correction=None, dev_tensors=None,
                              softmax_scale=w.scale, q_scale=inp.q_scale, k_scale=inp.k_scale,
                              v_scale=inp.v_scale, page_table=table, page_size=w.page_size,
                              kv_splits=kv_splits,
-                             kv_seqlens=w.seqlens if w.q_lens is not None else None)
+                             kv_seqlens=w.seqlens if w.q_lens is not None else None,
+                             v_dmajor=v_dmajor)
     params = bslp.make_params(w.alpha if alpha is None else alpha, w.sink, w.window, w.recent,
                               w.correction if correction is None else correction)
     bufs = bslp.Buffers(prob)

@@ -104,6 +104,23 @@ def test_page_table_validation():
     assert bslp.get_sizes(_problem(page_table=pt, page_size=256)).total_tokens == 1300
 
 
+def test_v_layout_validation():
+    # d-major V (fp8 only, pages of at least 64 tokens); other values refused
+    fp8 = dict(dtype="fp8", q_scale=0.5, k_scale=0.5, v_scale=0.5)
+    assert bslp.get_sizes(_problem(v_dmajor=True, **fp8)).kv_tokens == 1300
+    st, _ = _status(lambda: bslp.get_sizes(_problem(v_dmajor=True)))
+    assert st == 2  # bf16
+    pt = FakeTensor((2, 64))
+    st, _ = _status(lambda: bslp.get_sizes(_problem(v_dmajor=True, page_table=pt, page_size=16,
+                                                    **fp8)))
+    assert st == 2
+    assert bslp.get_sizes(_problem(v_dmajor=True, page_table=pt, page_size=64, **fp8)).kv_tokens == 1300
+    p = _problem(**fp8)
+    p.v_layout = 7
+    st, _ = _status(lambda: bslp.get_sizes(p))
+    assert st == 1
+
+
 @pytest.mark.parametrize("kw", [dict(alpha=-0.1), dict(alpha=float("inf")), dict(sink=-1),
                                 dict(correction=2)])
 def test_params_validation(kw):
