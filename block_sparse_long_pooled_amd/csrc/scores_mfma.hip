@@ -77,11 +77,17 @@ __device__ __forceinline__ float group_sum(float x) {
   return x + swz_xor<1>(x);
 }
 
-// Two-term split of a float into bf16 bit patterns, both rounded to
-// nearest even: x = hi + lo + r with |r| <= 2^-18 |x| (x - hi is exact).
-__device__ __forceinline__ void split2(float x, uint16_t& hi, uint16_t& lo) {
-  hi = f32_to_bf16(x);
-  lo = f32_to_bf16(x - bf16_to_f32(hi));
+// Two-term split of two floats into packed bf16 pairs, every term rounded to
+// nearest even by v_cvt_pk_bf16_f32: x = hi + lo + r with |r| <= 2^-18 |x|
+// (x - hi is exact).  Returns (hi pair, lo pair), element a in the low half.
+__device__ __forceinline__ uint2 split2_pair(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const bf2 h = __builtin_convertvector(f2{a, b}, bf2);
+  const uint32_t hu = __builtin_bit_cast(uint32_t, h);
+  const float ha = __uint_as_float(hu << 16), hb = __uint_as_float(hu & 0xffff0000u);
+  const bf2 l = __builtin_convertvector(f2{a - ha, b - hb}, bf2);
+  return make_uint2(hu, __builtin_bit_cast(uint32_t, l));
 }
 
 // 8 e4m3 codes (two little-endian words) as 8 bf16, exactly.  An e4m3 value
@@ -179,15 +185,20 @@ void scores_mfma_kernel(Plan p,
   // ---- kbar chunk staging: global float32 -> registers -> split bf16 in LDS
   float4 pf[PF];
   auto fetch = [&](int c) {
+    const bool full = (c + 1) * kChunk <= nJ;  // uniform: only the last chunk is partial
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int f = tid + i * NT;
       const int j = f / (D / 4);
       const int J = c * kChunk + j;
-      pf[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if ((F4 % NT == 0 || f < F4) && J < nJ)
-        pf[i] = *reinterpret_cast<const float4*>(kb_head + (int64_t)J * kb_stride +
-                                                 (f % (D / 4)) * 4);
+      const float4* src =
+          reinterpret_cast<const float4*>(kb_head + (int64_t)J * kb_stride + (f % (D / 4)) * 4);
+      if (full && (F4 % NT == 0 || f < F4)) {
+        pf[i] = *src;
+      } else {
+        pf[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if ((F4 % NT == 0 || f < F4) && J < nJ) pf[i] = *src;
+      }
     }
   };
   auto store = [&](int buf) {
@@ -197,15 +208,10 @@ void scores_mfma_kernel(Plan p,
       if (F4 % NT != 0 && f >= F4) break;
       const int j = f / (D / 4);
       const int d0 = (f % (D / 4)) * 4;
-      const float xv[4] = {pf[i].x, pf[i].y, pf[i].z, pf[i].w};
-      uint16_t hs[4], ls[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) split2(xv[e], hs[e], ls[e]);
+      const uint2 p01 = split2_pair(pf[i].x, pf[i].y), p23 = split2_pair(pf[i].z, pf[i].w);
       const int o = j * LD + d0;
-      *reinterpret_cast<uint2*>(&kb[buf][0][o]) =
-          make_uint2(hs[0] | ((uint32_t)hs[1] << 16), hs[2] | ((uint32_t)hs[3] << 16));
-      *reinterpret_cast<uint2*>(&kb[buf][1][o]) =
-          make_uint2(ls[0] | ((uint32_t)ls[1] << 16), ls[2] | ((uint32_t)ls[3] << 16));
+      *reinterpret_cast<uint2*>(&kb[buf][0][o]) = make_uint2(p01.x, p23.x);
+      *reinterpret_cast<uint2*>(&kb[buf][1][o]) = make_uint2(p01.y, p23.y);
     }
   };
 
