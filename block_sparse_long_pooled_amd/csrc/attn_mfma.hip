@@ -1,5 +1,6 @@
 // Stage 3 on the matrix cores: block-sparse causal online-softmax attention
-// with mean correction and PackGQA rows, bf16 or fp8 (e4m3) inputs
+// with mean correction and PackGQA rows, bf16 inputs (fp8 inputs take the
+// kernel of attn_fp8.hip)
 // ("FlashPrefill V2",
 // Sec. 3.1 last sentence, Sec. 3.2 / Fig. 3 correction path, PackGQA, CSR
 // and paged-KV paragraphs).  Written for gfx950 wave64 MFMA.
@@ -57,22 +58,6 @@ __device__ __forceinline__ int kperm(int key) {  // V^T column of a key
   return (key & ~15) | ((key & 4) << 1) | ((key & 8) >> 1) | (key & 3);
 }
 
-// Eight OCP e4m3 codes (two little-endian words) widened to eight bf16.  Every
-// e4m3 value is exact in bf16, and its bf16 bits are the top half of the
-// float32 bits, so a byte permute packs each pair without rounding.
-__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-  u32x4_t r;
-  r[0] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-  r[1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
-  r[3] = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
-  return r;
-}
-
 }  // namespace
 
 template <int D, int NW, int RT>
@@ -102,10 +87,9 @@ struct Prefetch {
   u32x4_t v1[AttnCfg<D, NW, RT>::VL];  // key 2a + 1
 };
 
-// Per-thread byte offsets of the 8-element pieces this thread fetches,
-// relative to the first row of a step (K/V rows and pooled rows share the
-// [row, Hkv, D] layout), for 2-byte (bf16) and 1-byte (e4m3) elements; fixed
-// for the whole unit.
+// Per-thread byte offsets of the 8-element (16-byte) pieces this thread
+// fetches, relative to the first row of a step (K/V rows and pooled rows
+// share the [row, Hkv, D] layout); fixed for the whole unit.
 template <int D, int NW, int RT>
 struct FetchOffsets {
   uint32_t k[AttnCfg<D, NW, RT>::KL];
@@ -114,7 +98,8 @@ struct FetchOffsets {
 };
 
 template <int D, int NW, int RT>
-__device__ __forceinline__ FetchOffsets<D, NW, RT> fetch_offsets(int hkv, int esize) {
+__device__ __forceinline__ FetchOffsets<D, NW, RT> fetch_offsets(int hkv) {
+  constexpr int esize = 2;  // bf16
   using C = AttnCfg<D, NW, RT>;
   constexpr int PAIRS = kKeys / 2;
   const int tid = threadIdx.x;
@@ -180,9 +165,8 @@ __device__ __forceinline__ void lds_load16(i32x4_t rsrc, uint32_t lds_addr, uint
                : "memory", "m0");
 }
 
-// Global -> registers for one step.  Exact steps read tokens key0.. of the
-// request (through the page table when K/V are paged), as bf16 or as e4m3
-// codes (8 bytes per piece, widened when written to LDS); correction steps
+// Global -> registers for one step.  Exact steps read bf16 tokens key0.. of
+// the request (through the page table when K/V are paged); correction steps
 // read the bf16 hi and lo rows of 64 pooled keys and their 64 pooled values.
 // When the step's rows are consecutive in memory (contiguous K/V, pages of at
 // least 64 tokens, pooled rows) the loads are raw buffer loads from one
@@ -191,10 +175,9 @@ __device__ __forceinline__ void lds_load16(i32x4_t rsrc, uint32_t lds_addr, uint
 // last correction chunk) read as zero.  With smaller pages every key's row is resolved on its own
 // and keys past the end re-read the last valid row.  Either way those keys'
 // scores are masked.
-template <int DT, int D, int NW, int RT, bool CORR>
+template <int D, int NW, int RT, bool CORR>
 __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
                                            const FetchOffsets<D, NW, RT>& off16,
-                                           const FetchOffsets<D, NW, RT>& off8,
                                            const CorrOffsets<D, NW, RT>& offc, const Step& st,
                                            const UnitCtx& u, const KVDesc& kv, int hkv,
                                            const void* k, const void* v,
@@ -203,8 +186,6 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
   using C = AttnCfg<D, NW, RT>;
   constexpr int PAIRS = kKeys / 2;
   const bool exact = st.kind == kExact;
-  const bool codes = DT == kFP8 && exact;  // 1-byte e4m3 elements
-  const int esize = codes ? 1 : 2;
   const int key0 = exact ? st.J * u.B + st.hf * kKeys : kCorrRows * st.c;
   const int last = exact ? min(kKeys, u.len - key0) - 1 : min(kCorrRows, u.I - key0) - 1;
   const bool paged = exact && kv.page_table != nullptr;
@@ -228,48 +209,33 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
       } else {
         row0 = (int64_t)u.kv_start + key0;
       }
-      kb0 = vb0 = (row0 * stride + (int64_t)u.h * D) * esize;
-      nrec_k = nrec_v = (last * (int)stride + D) * esize;
+      kb0 = vb0 = (row0 * stride + (int64_t)u.h * D) * 2;
+      nrec_k = nrec_v = (last * (int)stride + D) * 2;
     }
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         (void*)uniform_ptr(ksrc + kb0), (short)0, uni(nrec_k), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)uniform_ptr(vsrc + vb0), (short)0, uni(nrec_v), kRsrcWord3);
-    if (codes) {
 #pragma unroll
-      for (int i = 0; i < C::KL; ++i) {
-        const auto w = __builtin_amdgcn_raw_buffer_load_b64(rk, (int)off8.k[i], 0, 0);
-        pf.k[i] = u32x4_t{w[0], w[1], 0u, 0u};
-      }
+    for (int i = 0; i < C::KL; ++i)
+      pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(exact ? off16.k[i] : offc.k[i]),
+                                                      0, 0);
+    if (CORR && !exact) {
+      // the lo rows go straight to LDS, [chunk][key], between the K and the
+      // V loads of the step
+      const uint64_t a = reinterpret_cast<uint64_t>(ksrc + kb0);
+      const i32x4_t rw = {uni((int)(uint32_t)a), uni((int)(uint32_t)(a >> 32)), uni(nrec_k),
+                          kRsrcWord3};
+      const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t)kl_slot;
+      const int wave = uni(threadIdx.x >> 6);
 #pragma unroll
-      for (int i = 0; i < C::VL; ++i) {
-        const auto w0 = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)off8.v0[i], 0, 0);
-        const auto w1 = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)off8.v1[i], 0, 0);
-        pf.v0[i] = u32x4_t{w0[0], w0[1], 0u, 0u};
-        pf.v1[i] = u32x4_t{w1[0], w1[1], 0u, 0u};
-      }
-    } else {
+      for (int i = 0; i < C::CPW; ++i)
+        lds_load16(rw, uni((int)(base + (uint32_t)(wave + i * NW) * C::KCS)), offc.kl[i]);
+    }
 #pragma unroll
-      for (int i = 0; i < C::KL; ++i)
-        pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(exact ? off16.k[i] : offc.k[i]),
-                                                        0, 0);
-      if (CORR && !exact) {
-        // the lo rows go straight to LDS, [chunk][key], between the K and the
-        // V loads of the step
-        const uint64_t a = reinterpret_cast<uint64_t>(ksrc + kb0);
-        const i32x4_t rw = {uni((int)(uint32_t)a), uni((int)(uint32_t)(a >> 32)), uni(nrec_k),
-                            kRsrcWord3};
-        const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t)kl_slot;
-        const int wave = uni(threadIdx.x >> 6);
-#pragma unroll
-        for (int i = 0; i < C::CPW; ++i)
-          lds_load16(rw, uni((int)(base + (uint32_t)(wave + i * NW) * C::KCS)), offc.kl[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < C::VL; ++i) {
-        pf.v0[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off16.v0[i], 0, 0);
-        pf.v1[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off16.v1[i], 0, 0);
-      }
+    for (int i = 0; i < C::VL; ++i) {
+      pf.v0[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off16.v0[i], 0, 0);
+      pf.v1[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off16.v1[i], 0, 0);
     }
     return;
   }
@@ -293,34 +259,22 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
   for (int i = 0; i < C::KL; ++i) {
     const int f = min(tid + i * C::NT, C::KUN - 1);
     const int64_t e = krow[i] * stride + hoff + (f % C::KU) * 8;
-    if (codes) {
-      const uint2 w = *reinterpret_cast<const uint2*>(ksrc + e);
-      pf.k[i] = u32x4_t{w.x, w.y, 0u, 0u};
-    } else {
-      pf.k[i] = *reinterpret_cast<const u32x4_t*>(ksrc + 2 * e);
-    }
+    pf.k[i] = *reinterpret_cast<const u32x4_t*>(ksrc + 2 * e);
   }
 #pragma unroll
   for (int i = 0; i < C::VL; ++i) {
     const int un = min(tid + i * C::NT, C::VPN - 1) / PAIRS;
     const int64_t e0 = vrow0[i] * stride + hoff + un * 8, e1 = vrow1[i] * stride + hoff + un * 8;
-    if (codes) {
-      const uint2 w0 = *reinterpret_cast<const uint2*>(vsrc + e0);
-      const uint2 w1 = *reinterpret_cast<const uint2*>(vsrc + e1);
-      pf.v0[i] = u32x4_t{w0.x, w0.y, 0u, 0u};
-      pf.v1[i] = u32x4_t{w1.x, w1.y, 0u, 0u};
-    } else {
-      pf.v0[i] = *reinterpret_cast<const u32x4_t*>(vsrc + 2 * e0);
-      pf.v1[i] = *reinterpret_cast<const u32x4_t*>(vsrc + 2 * e1);
-    }
+    pf.v0[i] = *reinterpret_cast<const u32x4_t*>(vsrc + 2 * e0);
+    pf.v1[i] = *reinterpret_cast<const u32x4_t*>(vsrc + 2 * e1);
   }
 }
 
 // Registers -> LDS: K row-major, V transposed with permuted key columns; both
 // with padded rows so the 16-byte operand reads of 16 lanes hit distinct banks.
 template <int D, int NW, int RT, bool CORR>
-__device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, bool widen,
-                                           uint16_t* Ks, uint16_t* Vt) {
+__device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, uint16_t* Ks,
+                                           uint16_t* Vt) {
   using C = AttnCfg<D, NW, RT>;
   const int tid = threadIdx.x;
 #pragma unroll
@@ -328,8 +282,7 @@ __device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, bool w
     const int f = tid + i * C::NT;
     if (C::KUN % C::NT != 0 && f >= C::KUN) break;
     const int key = f / C::KU, un = f % C::KU;
-    *reinterpret_cast<u32x4_t*>(Ks + key * C::KLD + un * 8) =
-        widen ? e4m3x8_to_bf16x8(pf.k[i][0], pf.k[i][1]) : pf.k[i];
+    *reinterpret_cast<u32x4_t*>(Ks + key * C::KLD + un * 8) = pf.k[i];
   }
 #pragma unroll
   for (int i = 0; i < C::VL; ++i) {
@@ -339,8 +292,7 @@ __device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, bool w
     // wave then fall in distinct banks (with 16 dims fastest they collide)
     const int a = s % (kKeys / 2), un = s / (kKeys / 2);
     const int col = kperm(2 * a);  // even; the pair stays adjacent
-    const u32x4_t w0 = widen ? e4m3x8_to_bf16x8(pf.v0[i][0], pf.v0[i][1]) : pf.v0[i];
-    const u32x4_t w1 = widen ? e4m3x8_to_bf16x8(pf.v1[i][0], pf.v1[i][1]) : pf.v1[i];
+    const u32x4_t w0 = pf.v0[i], w1 = pf.v1[i];
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
       const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
@@ -497,11 +449,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ items,
     int* __restrict__ queue) {
   using C = AttnCfg<D, NW, RT>;
+  static_assert(DT == kBF16, "bf16 inputs only; fp8 takes attn_fp8_kernel");
   if constexpr (!CORR) correction = 0;  // compiled without correction steps
-  if (p.dscale) {  // fp8 scales kept on the device
-    c *= p.dscale[0] * p.dscale[1];
-    out_scale = p.dscale[2];
-  }
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKeys * C::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VLD];
   // correction steps: the lo rows of the pooled keys, a ring of three slots
@@ -546,29 +495,13 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     qpos[rt] = q0 + (valid[rt] ? r / p.g : 0);
     hqs[rt] = h * p.g + (valid[rt] ? r % p.g : 0);
     const int64_t qoff = (q_row(s, qpos[rt]) * p.hq + hqs[rt]) * D;
-    if constexpr (DT == kFP8) {
-      // every lane loads (a padding row reads the tile's first row), so the
-      // loads issue back to back instead of one round trip per widening
-      uint2 cw[C::KS];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        cw[ks] = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(q) + qoff + ks * 16 +
-                                                 half * 8);
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        u32x4_t w = e4m3x8_to_bf16x8(cw[ks].x, cw[ks].y);
-        if (!valid[rt]) w = u32x4_t{0u, 0u, 0u, 0u};
-        qf[rt][ks] = __builtin_bit_cast(bf16x8_t, w);
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (valid[rt])
-          w = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(q) + qoff + ks * 16 +
-                                                half * 8);
-        qf[rt][ks] = __builtin_bit_cast(bf16x8_t, w);
-      }
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (valid[rt])
+        w = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(q) + qoff + ks * 16 +
+                                              half * 8);
+      qf[rt][ks] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
 
@@ -600,15 +533,14 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   }
   const float bias = __log2f((float)p.B);  // corrected blocks are full blocks
 
-  const FetchOffsets<D, NW, RT> off16 = fetch_offsets<D, NW, RT>(p.hkv, 2);
-  const FetchOffsets<D, NW, RT> off8 = fetch_offsets<D, NW, RT>(p.hkv, DT == kFP8 ? 1 : 2);
+  const FetchOffsets<D, NW, RT> off16 = fetch_offsets<D, NW, RT>(p.hkv);
   const CorrOffsets<D, NW, RT> offc = corr_offsets<D, NW, RT>(p.hkv);
   Prefetch<D, NW, RT> pf;
   Step cur = first_step(u, idx, selbits, correction);
   if (cur.kind != kDone) {
-    fetch_step<DT, D, NW, RT, CORR>(pf, off16, off8, offc, cur, u, kv, p.hkv, k, v, kb2, vb16,
+    fetch_step<D, NW, RT, CORR>(pf, off16, offc, cur, u, kv, p.hkv, k, v, kb2, vb16,
                                     Kl[0]);
-    store_step<D, NW, RT, CORR>(pf, DT == kFP8 && cur.kind == kExact, Ks[0], Vt[0]);
+    store_step<D, NW, RT, CORR>(pf, Ks[0], Vt[0]);
   }
   uniform(cur);
   // the query rows and the first step have arrived; saying so here keeps the
@@ -618,7 +550,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   if (cur.kind != kDone) advance(nxt, u, idx, selbits, correction);
   uniform(nxt);
   if (nxt.kind != kDone)
-    fetch_step<DT, D, NW, RT, CORR>(pf, off16, off8, offc, nxt, u, kv, p.hkv, k, v, kb2, vb16,
+    fetch_step<D, NW, RT, CORR>(pf, off16, offc, nxt, u, kv, p.hkv, k, v, kb2, vb16,
                                     Kl[1]);
   int buf = 0;
   int ls = 0;  // Kl slot of step n (n+1 and n+2 follow, modulo 3)
@@ -636,10 +568,10 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
       uniform(nn);
     }
     if (nxt.kind != kDone)
-      store_step<D, NW, RT, CORR>(pf, DT == kFP8 && nxt.kind == kExact, Ks[buf ^ 1], Vt[buf ^ 1]);
+      store_step<D, NW, RT, CORR>(pf, Ks[buf ^ 1], Vt[buf ^ 1]);
     // slot ls + 2 held step n-1, which every wave finished before the barrier
     if (nn.kind != kDone)
-      fetch_step<DT, D, NW, RT, CORR>(pf, off16, off8, offc, nn, u, kv, p.hkv, k, v, kb2, vb16,
+      fetch_step<D, NW, RT, CORR>(pf, off16, offc, nn, u, kv, p.hkv, k, v, kb2, vb16,
                                       Kl[ls == 0 ? 2 : ls - 1]);
     if (wave_active) {
       int mode, key0 = 0;
@@ -852,34 +784,26 @@ __global__ __launch_bounds__(1024) void split_items_kernel(Plan p, const int32_t
   }
 }
 
-// float32 pooled means -> bf16 for the correction steps, divided by the
-// per-tensor K / V scales of fp8 inputs so that they share the scale of the
-// e4m3 codes.  Keys become the pair hi = bf16(x), lo = bf16(x - hi) (x - hi is
-// exact in float32, so hi + lo is x to within 2^-18 |x|), stored as
-// [pooled row, {hi, lo}, Hkv, D]; values are rounded once, [pooled row, Hkv,
-// D].  n8 = 8-element groups per tensor, row8 = groups per pooled row.
+// float32 pooled means -> bf16 for the correction steps.  Keys become the pair
+// hi = bf16(x), lo = bf16(x - hi) (x - hi is exact in float32, so hi + lo is
+// x to within 2^-18 |x|), stored as [pooled row, {hi, lo}, Hkv, D]; values are
+// rounded once, [pooled row, Hkv, D].  n8 = 8-element groups per tensor,
+// row8 = groups per pooled row.
 __global__ __launch_bounds__(256) void pooled_to_bf16_kernel(const float* __restrict__ kbar,
                                                             const float* __restrict__ vbar,
-                                                            int64_t n8, int row8, float k_inv,
-                                                            float v_inv,
-                                                            const float* __restrict__ dscale,
+                                                            int64_t n8, int row8,
                                                             uint16_t* __restrict__ kb2,
                                                             uint16_t* __restrict__ vb16) {
-  if (dscale) {
-    k_inv = 1.f / dscale[1];
-    v_inv = 1.f / dscale[2];
-  }
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= 2 * n8) return;
   const bool is_v = i >= n8;
   const int64_t j = is_v ? i - n8 : i;
   const float* src = (is_v ? vbar : kbar) + 8 * j;
-  const float sc = is_v ? v_inv : k_inv;
   float x[8];
   const float4 a = *reinterpret_cast<const float4*>(src);
   const float4 bq = *reinterpret_cast<const float4*>(src + 4);
-  x[0] = a.x * sc; x[1] = a.y * sc; x[2] = a.z * sc; x[3] = a.w * sc;
-  x[4] = bq.x * sc; x[5] = bq.y * sc; x[6] = bq.z * sc; x[7] = bq.w * sc;
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = bq.x; x[5] = bq.y; x[6] = bq.z; x[7] = bq.w;
   u32x4_t hi, lo;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -998,13 +922,12 @@ static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs&
   if (n > 0 && a.correction && !a.dense) {
     const int64_t n8 = (int64_t)(n / 8);
     hipLaunchKernelGGL(pooled_to_bf16_kernel, dim3((unsigned)((2 * n8 + 255) / 256)), dim3(256),
-                       0, st, a.kbar, a.vbar, n8, p.hkv * p.d / 8, 1.f / a.k_scale,
-                       1.f / a.v_scale, p.dscale, kb2, vb16);
+                       0, st, a.kbar, a.vbar, n8, p.hkv * p.d / 8, kb2, vb16);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // logits of the codes: softmax_scale * q_scale * k_scale, in units of log2
-  const float c = (float)((double)a.lscale * (double)a.k_scale * 1.4426950408889634);
+  // logits in units of log2
+  const float c = (float)((double)a.lscale * 1.4426950408889634);
   const int splits = a.splits;
   const int corr = a.correction && !a.dense;
   if (splits == 1) {
