@@ -77,7 +77,7 @@ class Sizes(ctypes.Structure):
     ]
 
 
-EXPORTS = ("bslp_get_sizes", "bslp_block_scores", "bslp_pool_kv", "bslp_score_blocks",
+EXPORTS = ("bslp_get_sizes", "bslp_workspace_bytes", "bslp_block_scores", "bslp_pool_kv", "bslp_score_blocks",
            "bslp_select_blocks",
            "bslp_sparse_prefill_attn", "bslp_sparse_prefill_attn_noalloc",
            "bslp_dense_prefill_attn", "bslp_quantize_e4m3", "bslp_status_string",
@@ -99,6 +99,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P = ctypes.POINTER
     vp = ctypes.c_void_p
     lib.bslp_get_sizes.argtypes = [P(Problem), P(Sizes)]
+    lib.bslp_workspace_bytes.argtypes = [P(Problem)]
+    lib.bslp_workspace_bytes.restype = ctypes.c_size_t
     lib.bslp_block_scores.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, vp]
     lib.bslp_pool_kv.argtypes = [P(Problem), vp, vp, vp, vp, vp]
     lib.bslp_score_blocks.argtypes = [P(Problem), vp, vp, vp, vp]
@@ -189,6 +191,11 @@ def get_sizes(problem: Problem) -> Sizes:
     s = Sizes()
     _check(load_library().bslp_get_sizes(ctypes.byref(problem), ctypes.byref(s)))
     return s
+
+
+def workspace_bytes(problem) -> int:
+    """Bytes of workspace bslp_sparse_prefill_attn needs (0: invalid problem)."""
+    return int(load_library().bslp_workspace_bytes(ctypes.byref(problem)))
 
 
 def block_scores(problem, q, k, v, kbar, vbar, scores, stream=None):

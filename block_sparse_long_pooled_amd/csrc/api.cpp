@@ -209,12 +209,12 @@ bslp_status sparse_attn(const bslp_problem* problem, const bslp_select_params* p
     if (e != hipSuccess) return hip_result(e, what);
   } else {
     if (workspace_bytes < need)
-      return fail(BSLP_ERR_INVALID_ARG, "workspace_bytes " + std::to_string(workspace_bytes) +
+      return fail(BSLP_ERR_WORKSPACE, "workspace_bytes " + std::to_string(workspace_bytes) +
                                             " is below the " + std::to_string(need) +
                                             " bytes bslp_get_sizes reports");
-    if (need > 0 && !workspace) return fail(BSLP_ERR_INVALID_ARG, "workspace is NULL");
+    if (need > 0 && !workspace) return fail(BSLP_ERR_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) % 16)
-      return fail(BSLP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+      return fail(BSLP_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   }
   bslp::AttnArgs a{q, k, v, kbar, vbar, cu, idx, out, lse, workspace,
                    problem->softmax_scale * host_scale(problem, 0), host_scale(problem, 1),
@@ -240,6 +240,12 @@ bslp_status bslp_get_sizes(const bslp_problem* problem, bslp_sizes* out) {
   out->workspace_bytes = (int64_t)bslp::attn_workspace_bytes(
       plan, bslp::attn_splits(plan, problem->dtype, problem->kv_splits));
   return BSLP_OK;
+}
+
+size_t bslp_workspace_bytes(const bslp_problem* problem) {
+  bslp_sizes sz;
+  if (bslp_get_sizes(problem, &sz) != BSLP_OK) return 0;
+  return (size_t)sz.workspace_bytes;
 }
 
 bslp_status bslp_block_scores(const bslp_problem* problem, const void* q, const void* k,
@@ -365,6 +371,7 @@ const char* bslp_status_string(bslp_status status) {
     case BSLP_ERR_INVALID_ARG: return "invalid argument";
     case BSLP_ERR_UNSUPPORTED: return "unsupported";
     case BSLP_ERR_HIP: return "HIP error";
+    case BSLP_ERR_WORKSPACE: return "workspace";
   }
   return "unknown status";
 }

@@ -64,7 +64,8 @@ typedef enum bslp_status {
   BSLP_OK = 0,
   BSLP_ERR_INVALID_ARG = 1, /* null pointer, inconsistent shape, bad value  */
   BSLP_ERR_UNSUPPORTED = 2, /* valid but not built (head_dim, block, limits) */
-  BSLP_ERR_HIP = 3          /* a HIP launch or runtime call failed          */
+  BSLP_ERR_HIP = 3,         /* a HIP launch or runtime call failed          */
+  BSLP_ERR_WORKSPACE = 4    /* workspace NULL, too small or misaligned      */
 } bslp_status;
 
 typedef enum bslp_dtype {
@@ -163,6 +164,14 @@ typedef struct bslp_sizes {
 /* Validates `problem` and fills `out`.  Host only; no HIP call. */
 bslp_status bslp_get_sizes(const bslp_problem* problem, bslp_sizes* out);
 
+/* The workspace bslp_sparse_prefill_attn needs for `problem`, in bytes (the
+ * workspace_bytes of bslp_get_sizes); 0 when the problem is invalid, with the
+ * reason in bslp_last_error().  Host only; no HIP call.  The workspace is
+ * reused by every layer of a forward pass (the pages build per-forward
+ * metadata once, with no allocator round trip), so one query per shape is
+ * enough. */
+size_t bslp_workspace_bytes(const bslp_problem* problem);
+
 /* Stage 1: pooled means and block scores.
  *
  * Pooling (FlashPrefill V2, Sec. 3.1; pooled values for Sec. 3.2):
@@ -252,10 +261,13 @@ bslp_status bslp_select_blocks(const bslp_problem* problem, const bslp_select_pa
  * [Hq, T] or NULL.  A row that sees no key gets O = 0 and LSE = -inf.
  * kbar / vbar / cu / idx are the outputs of stages 1 and 2 for the same
  * problem.  Only params->mean_correction is read.
- * workspace: device scratch of at least bslp_sizes.workspace_bytes bytes,
+ * workspace: device scratch of at least bslp_workspace_bytes(problem) bytes,
  * 16-byte aligned, owned by the caller; its contents on entry do not matter
  * and are overwritten (the call keeps bf16 copies of kbar, as hi + lo pairs,
- * and of vbar there).  Calls that overlap in time must not share a workspace. */
+ * and of vbar there; for fp8 the quantised pooled codes; with KV splits the
+ * partial results).  A NULL (when bytes are needed), short or misaligned
+ * workspace is BSLP_ERR_WORKSPACE, before any launch.  Calls that overlap in
+ * time must not share a workspace. */
 bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,
                                      const bslp_select_params* params, const void* q,
                                      const void* k, const void* v, const float* kbar,

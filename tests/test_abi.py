@@ -169,21 +169,30 @@ def test_status_strings():
 
 
 def test_attention_workspace_validated_before_launch():
+    # NULL, short and misaligned workspaces are BSLP_ERR_WORKSPACE (4)
     p = _problem()
     need = bslp.get_sizes(p).workspace_bytes
+    assert bslp.workspace_bytes(p) == need > 0
     params = bslp.make_params(0.05)
     t = FakeTensor()
     st, d = _status(lambda: bslp.sparse_prefill_attn(p, params, t, t, t, t, t, t, t, t, t,
                                                      workspace=FakeTensor(nbytes=need - 1),
                                                      stream=0))
-    assert st == 1 and "workspace" in d
+    assert st == 4 and "workspace" in d
     st, d = _status(lambda: bslp.sparse_prefill_attn(p, params, t, t, t, t, t, t, t, t, t,
                                                      workspace=None, stream=0))
-    assert st == 1 and "workspace" in d
+    assert st == 4 and "workspace" in d
     st, d = _status(lambda: bslp.sparse_prefill_attn(
         p, params, t, t, t, t, t, t, t, t, t,
         workspace=FakeTensor(nbytes=need, ptr=0x1008), stream=0))
-    assert st == 1 and "aligned" in d
+    assert st == 4 and "aligned" in d
+    assert bslp.load_library().bslp_status_string(4) == b"workspace"
+
+
+def test_workspace_bytes_of_an_invalid_problem_is_zero():
+    p = _problem(head_dim=80)
+    assert bslp.workspace_bytes(p) == 0
+    assert b"head_dim" in bslp.load_library().bslp_last_error()
 
 
 def test_dense_attention_validated_before_launch():
