@@ -97,7 +97,7 @@ hipError_t launch_pool_v_dmajor(const Plan& p, const KVDesc& kv, const void* v, 
 constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
 hipError_t noalloc_scratch(void** out);
 
-// bf16 and fp8 inputs on the matrix cores (fp8 codes widen exactly to bf16).
+// bf16 inputs on the matrix cores (fp8 inputs take launch_attn_fp8).
 hipError_t launch_attn_mfma(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
                             hipStream_t st);
 

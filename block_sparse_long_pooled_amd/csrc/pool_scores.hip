@@ -15,6 +15,7 @@ namespace bslp {
 // and the groups are combined in fixed order, so results are deterministic.
 // HBM-bound: the block's K (or V) rows are read once.
 constexpr int kPoolThreads = 256;
+constexpr int kRowsInFlight = 8;  // token rows a thread loads before adding them
 
 template <int D>
 constexpr int pool_heads() { return kPoolThreads * 8 / D; }  // heads per workgroup
@@ -45,30 +46,32 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Plan p, KVDesc kv,
   const typename Elem<DT>::T* x = is_v ? v : k;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (active) {
-    // four rows' loads in flight at a time, added in row order as one by one
+    // kRowsInFlight rows' loads in flight at a time, added in row order as
+    // one by one (the sum is the same as a row-by-row loop's)
+    constexpr int U = kRowsInFlight;
     int r = rg;
-    for (; r + 3 * rg_n < cnt; r += 4 * rg_n) {
-      // all four rows first (their page-table entries in one batch of loads),
+    for (; r + (U - 1) * rg_n < cnt; r += U * rg_n) {
+      // all U rows first (their page-table entries in one batch of loads),
       // then the data
-      int64_t rows[4];
+      int64_t rows[U];
       if (kv.page_table != nullptr) {
-        int32_t phys[4];
+        int32_t phys[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < U; ++u)
           phys[u] = kv.page_table[(int64_t)b * kv.max_pages + ((j0 + r + u * rg_n) >> kv.page_shift)];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < U; ++u)
           rows[u] = ((int64_t)phys[u] << kv.page_shift) |
                     (int64_t)((j0 + r + u * rg_n) & ((1 << kv.page_shift) - 1));
       } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) rows[u] = (int64_t)s.kv_start + j0 + r + u * rg_n;
+        for (int u = 0; u < U; ++u) rows[u] = (int64_t)s.kv_start + j0 + r + u * rg_n;
       }
-      float e[4][8];
+      float e[U][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) load8<DT>(x, (rows[u] * p.hkv + h0) * D + col8 * 8, e[u]);
+      for (int u = 0; u < U; ++u) load8<DT>(x, (rows[u] * p.hkv + h0) * D + col8 * 8, e[u]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += e[u][i];
       }
