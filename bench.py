@@ -213,11 +213,14 @@ def percentile(x, q):
 
 
 def measure(bslp, torch, w, inp, steps: int, warmup: int, kv_splits: int, evict_bytes: int,
-            v_dmajor: bool = False):
+            v_dmajor: bool = False, evict_write: bool = False):
     """Runs the layer `warmup + steps` times with HIP events around each
     kernel launch on the launch stream; between steps a scratch buffer of
-    evict_bytes is written so the next step starts with cold caches (MALL and
-    L2).  Returns per-step stage times (ms) and the buffers of the last step."""
+    evict_bytes is read (or, with evict_write, written) so the next step
+    starts with cold caches (MALL and L2).  Reading evicts without leaving
+    dirty lines, whose write-back would otherwise fall on the step's first
+    kernel.  Returns per-step stage times (ms) and the buffers of the last
+    step."""
     dev = torch.device("cuda")
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     if v_dmajor:  # [Hkv, d, kv tokens] (contiguous K/V only here)
@@ -233,7 +236,15 @@ def measure(bslp, torch, w, inp, steps: int, warmup: int, kv_splits: int, evict_
     bufs = bslp.Buffers(prob)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    scratch = torch.empty(max(1, evict_bytes), dtype=torch.uint8, device=dev)
+    scratch = torch.zeros(max(4, evict_bytes) // 4, dtype=torch.float32, device=dev)
+
+    def evict(i):
+        if not evict_bytes:
+            return
+        if evict_write:
+            scratch.fill_(float(i & 255))
+        else:
+            torch.sum(scratch)  # reads every byte once
 
     def step(ev=None):
         rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
@@ -250,15 +261,13 @@ def measure(bslp, torch, w, inp, steps: int, warmup: int, kv_splits: int, evict_
         rec(4)
 
     for i in range(warmup):
-        if evict_bytes:
-            scratch.fill_(i & 255)
+        evict(i)
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        if evict_bytes:
-            scratch.fill_((i + 1) & 255)  # outside the timed kernels
+        evict(i + 1)  # outside the timed kernels
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -325,7 +334,10 @@ def main():
     ap.add_argument("--kv-splits", type=int, default=0,
                     help="attention KV splits: 0 automatic, 1 none, 2..16 forced")
     ap.add_argument("--evict-mib", type=int, default=512,
-                    help="scratch written between timed steps to evict MALL and L2 (0: none)")
+                    help="scratch read between timed steps to evict MALL and L2 (0: none)")
+    ap.add_argument("--evict-write", action="store_true",
+                    help="write the eviction scratch instead of reading it (its dirty lines are "
+                         "then written back during the next step's first kernel)")
     ap.add_argument("--quant-reps", type=int, default=5,
                     help="timed online e4m3 quantisations of Q for bf16 workloads (0 skips)")
     ap.add_argument("--dense-reps", type=int, default=3,
@@ -352,7 +364,8 @@ def main():
     t_gen = time.time() - t_gen
     evict = args.evict_mib << 20
     cdt = COMPUTE_DTYPE[w.dtype]
-    m = measure(bslp, torch, w, inp, args.steps, args.warmup, args.kv_splits, evict)
+    m = measure(bslp, torch, w, inp, args.steps, args.warmup, args.kv_splits, evict,
+                evict_write=args.evict_write)
     sm = summarize(w, m, PEAK_TFLOPS[cdt])
     ms_step = sm["layer_ms"]["median"]
     f_dense = dense_flops(w)
@@ -382,7 +395,7 @@ def main():
         },
         "ms_per_layer": ms_step,
         "timing": {"protocol": f"HIP events around each kernel launch on the launch stream; "
-                               f"{args.evict_mib} MiB scratch written between steps (cold MALL/L2); "
+                               f"{args.evict_mib} MiB scratch {'written' if args.evict_write else 'read'} between steps (cold MALL/L2); "
                                f"median over {args.steps} steps",
                    "layer_ms": sm["layer_ms"], "stages_p90_ms": sm["stages_p90_ms"],
                    "wall_s": m["wall"]},
@@ -453,7 +466,8 @@ def main():
         torch.cuda.empty_cache()
         w8 = CONFIGS["128k-fp8"]
         inp8 = make_inputs(w8, args.seed)
-        m8 = measure(bslp, torch, w8, inp8, args.fp8_steps, 2, args.kv_splits, evict)
+        m8 = measure(bslp, torch, w8, inp8, args.fp8_steps, 2, args.kv_splits, evict,
+                     evict_write=args.evict_write)
         s8 = summarize(w8, m8, PEAK_TFLOPS["fp8"])
         res["fp8_128k"] = {
             "workload": w8.name, "density": round(s8["density"], 5),
@@ -469,7 +483,7 @@ def main():
             del m8
             torch.cuda.empty_cache()
             md = measure(bslp, torch, w8, inp8, args.fp8_steps, 2, args.kv_splits, evict,
-                         v_dmajor=True)
+                         v_dmajor=True, evict_write=args.evict_write)
             sd = summarize(w8, md, PEAK_TFLOPS["fp8"])
             res["fp8_128k"]["v_dmajor"] = {"ms_per_layer": sd["layer_ms"]["median"],
                                            "stages_ms": sd["stages_ms"],
