@@ -28,9 +28,11 @@
 // v_permlane32_swap, and the waves' partials (m, S) meet in LDS, where each
 // wave merges 32/NW of the chunk's blocks over the NW partials with
 // shuffles, so no wave does more of it than another.  The per-block maxima
-// m_J stay in LDS and the sums S_J in the score row; at the end every
-// thread takes part in M_I = max_J m_J, the total sum_J S_J 2^(m_J - M_I)
-// (float64) and the scores S_J 2^(m_J - M_I) / total.
+// m_J stay in LDS and the sums S_J in the score row.  Each combine group
+// also keeps a running pair (largest m_J so far, float64 sum of its
+// S_J 2^(m_J - that maximum)); at the end every thread merges the 32 pairs
+// into M_I = max_J m_J and the total sum_J S_J 2^(m_J - M_I), and writes
+// the scores S_J 2^(m_J - M_I) / total.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -42,6 +44,15 @@ typedef float sf32x16_t __attribute__((ext_vector_type(16)));
 namespace {
 
 constexpr int kChunk = 32;  // key blocks per chunk = MFMA N
+constexpr int kScRsrcWord3 = 0x00020000;  // raw buffer descriptor, 32-bit data format
+
+__device__ __forceinline__ int sc_uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ const float* sc_uniform_ptr(const float* p) {
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)sc_uni((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)sc_uni((int)(uint32_t)(x >> 32));
+  return reinterpret_cast<const float*>(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -117,6 +128,7 @@ void scores_mfma_kernel(Plan p,
                                                               const float* __restrict__ kbar,
                                                               float c2, float* __restrict__ scores) {
   if (p.dscale) c2 *= p.dscale[0];  // fp8 q scale kept on the device
+  c2 = __builtin_bit_cast(float, sc_uni(__builtin_bit_cast(int, c2)));  // uniform: a scalar register
   constexpr int NT = NW * 64;
   constexpr int KS = D / 16;            // k-steps of 16 dims
   constexpr int LD = D + 8;             // padded LDS row (bf16), 16-byte multiple
@@ -125,8 +137,8 @@ void scores_mfma_kernel(Plan p,
   __shared__ __attribute__((aligned(16))) uint16_t kb[2][2][kChunk * LD];
   __shared__ float part_m[2][NW][kChunk];
   __shared__ float part_s[2][NW][kChunk];
-  __shared__ float red_m[NW];
-  __shared__ double red_s[NW];
+  __shared__ float red_m[kChunk];
+  __shared__ double red_s[kChunk];
   extern __shared__ float dyn[];  // m_J[nch * 32]
 
   const int tid = threadIdx.x;
@@ -182,26 +194,28 @@ void scores_mfma_kernel(Plan p,
     }
   }
 
-  // ---- kbar chunk staging: global float32 -> registers -> split bf16 in LDS
-  float4 pf[PF];
-  auto fetch = [&](int c) {
-    const bool full = (c + 1) * kChunk <= nJ;  // uniform: only the last chunk is partial
+  // ---- kbar chunk staging: global float32 -> registers -> split bf16 in LDS.
+  // Raw buffer loads from one scalar descriptor per chunk: the descriptor
+  // ends after the chunk's last block, so the rows past it read as zero.
+  uint32_t foff[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int f = tid + i * NT;
-      const int j = f / (D / 4);
-      const int J = c * kChunk + j;
-      const float4* src =
-          reinterpret_cast<const float4*>(kb_head + (int64_t)J * kb_stride + (f % (D / 4)) * 4);
-      if (full && (F4 % NT == 0 || f < F4)) {
-        pf[i] = *src;
-      } else {
-        pf[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if ((F4 % NT == 0 || f < F4) && J < nJ) pf[i] = *src;
-      }
-    }
+  for (int i = 0; i < PF; ++i) {
+    const int f = tid + i * NT;
+    foff[i] = (F4 % NT == 0 || f < F4)
+                  ? (uint32_t)(f / (D / 4)) * (uint32_t)kb_stride * 4u + (uint32_t)(f % (D / 4)) * 16u
+                  : 0x80000000u;  // past every descriptor: reads zero, never stored
+  }
+  float4 pf[PF];
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+    const int last = min(kChunk, nJ - c * kChunk) - 1;
+    const float* base = kb_head + (int64_t)c * kChunk * kb_stride;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)sc_uniform_ptr(base), (short)0, sc_uni((last * (int)kb_stride + D) * 4), kScRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      pf[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)foff[i], 0, 0));
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int f = tid + i * NT;
@@ -223,18 +237,29 @@ void scores_mfma_kernel(Plan p,
   // the chunk, a lane (of each half) the partial of row wave sw for block jl,
   // and groups of NW lanes reduce (max, then the rescaled sum) in a fixed
   // butterfly order.  The partials are double buffered, so the merge of
-  // chunk c-1 runs during chunk c, beside its matrix work.
+  // chunk c-1 runs during chunk c, beside its matrix work.  Every lane of a
+  // group also folds the block into a running pair (rm, rs): the largest
+  // block maximum so far and the sum of S_J 2^(m_J - rm) over its blocks.
+  constexpr int BPW = kChunk / NW;
+  static_assert(NW == 4 || NW == 8 || NW == 16, "combine groups");
+  int jl = wave * BPW + jj / NW, sw = jj % NW;
+  float rm = -INFINITY;
+  double rs = 0.0;
   auto combine = [&](int cc) __attribute__((always_inline)) {
-    constexpr int BPW = kChunk / NW;
-    static_assert(NW == 4 || NW == 8 || NW == 16, "combine groups");
-    const int jl = wave * BPW + jj / NW, sw = jj % NW;
     const float pmv = part_m[cc & 1][sw][jl], psv = part_s[cc & 1][sw][jl];
     const float m = group_max<NW>(pmv);
     const float S = group_sum<NW>(psv * __builtin_amdgcn_exp2f(pmv - (m == -INFINITY ? 0.f : m)));
     const int J = cc * kChunk + jl;
-    if (half == 0 && sw == 0 && J < nJ) {
-      mJ[J] = m;
-      row_out[J] = S;
+    if (J < nJ) {
+      const float nm = fmaxf(rm, m);
+      const float ref = nm == -INFINITY ? 0.f : nm;
+      rs = rs * (double)__builtin_amdgcn_exp2f(rm - ref) +
+           (double)S * (double)__builtin_amdgcn_exp2f(m - ref);
+      rm = nm;
+      if (half == 0 && sw == 0) {
+        mJ[J] = m;
+        row_out[J] = S;
+      }
     }
   };
 
@@ -275,13 +300,18 @@ void scores_mfma_kernel(Plan p,
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[t][i]);
         }
       } else {
-        const bool okJ = J < nJ;
+        // rows r < R of the lane: element i of row tile t is row
+        // row0 + 32 t + 8 (i >> 2) + 4 half + (i & 3).  The limit is made
+        // opaque here, so the 32 comparisons are not hoisted out of the chunk
+        // loop as scalar lane masks.
+        int t0 = threadIdx.x;
+        asm volatile("" : "+v"(t0));
+        const int lim = J < nJ ? R - (t0 >> 6) * (RT * 32) - ((t0 >> 5) & 1) * 4 : 0;
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int r = row0 + t * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            acc[t][i] = (okJ && r < R) ? acc[t][i] : -INFINITY;
+            acc[t][i] = t * 32 + (i >> 2) * 8 + (i & 3) < lim ? acc[t][i] : -INFINITY;
             mx = fmaxf(mx, acc[t][i]);
           }
         }
@@ -304,32 +334,35 @@ void scores_mfma_kernel(Plan p,
     if (c + 1 < nch) store(buf ^ 1);
     __syncthreads();
   }
+  // the combine indices again, from an opaque copy of the thread index: the
+  // values from before the loop would otherwise stay live through it
+  {
+    int t1 = threadIdx.x;
+    asm volatile("" : "+v"(t1));
+    jl = (t1 >> 6) * BPW + (t1 & 31) / NW;
+    sw = (t1 & 31) % NW;
+  }
   combine(nch - 1);
+  // M_I and the total sum_J S_J 2^(m_J - M_I) from the 32 running pairs (one
+  // per combine group, merged by every thread in the same order), then every
+  // score.  The barrier also makes the S_J stores visible.
+  if (half == 0 && sw == 0) {
+    red_m[jl] = rm;
+    red_s[jl] = rs;
+  }
   __syncthreads();
-  // M_I, then the total in float64 (per-thread strided, butterflies, waves in
-  // order), then every score; the barrier makes the S_J stores visible
-  float mloc = -INFINITY;
-  for (int J = tid; J < nJ; J += NT) mloc = fmaxf(mloc, mJ[J]);
+  float M = -INFINITY;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
-  if (lane == 0) red_m[wave] = mloc;
-  __syncthreads();
-  float Mf = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) Mf = fmaxf(Mf, red_m[w]);
-  const double M = (double)Mf;
-  double tloc = 0.0;
-  for (int J = tid; J < nJ; J += NT) tloc += (double)row_out[J] * exp2((double)mJ[J] - M);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) tloc += __shfl_xor(tloc, off);
-  if (lane == 0) red_s[wave] = tloc;
-  __syncthreads();
+  for (int k = 0; k < kChunk; ++k) M = fmaxf(M, red_m[k]);
   double tot = 0.0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) tot += red_s[w];
-  const double inv = 1.0 / tot;
+  for (int k = 0; k < kChunk; ++k) {
+    const float mk = red_m[k];
+    if (mk != -INFINITY) tot += red_s[k] * (double)__builtin_amdgcn_exp2f(mk - M);
+  }
+  const float inv = (float)(1.0 / tot);
   for (int J = tid; J < nJ; J += NT)
-    row_out[J] = (float)((double)row_out[J] * exp2((double)mJ[J] - M) * inv);
+    row_out[J] = row_out[J] * __builtin_amdgcn_exp2f(mJ[J] - M) * inv;
 }
 
 template <int DT, int D, int RT, int NW>
