@@ -118,11 +118,11 @@ __device__ __forceinline__ uint4 widen_e4m3x8(uint2 u) {
 
 }  // namespace
 
-// Two row tiles per wave at 16 waves (1024-row tiles) or at 8 waves for bf16
-// fit in 128 VGPRs, i.e. 4 waves per SIMD: two 8-wave workgroups share a CU,
-// so one workgroup's per-chunk barrier and combine overlap the other's MFMAs.
+// Two row tiles per wave at 8 waves (512-row tiles) fit in 128 VGPRs, i.e.
+// 4 waves per SIMD: two 8-wave workgroups share a CU, so one workgroup's
+// per-chunk barrier and combine overlap the other's MFMAs.
 template <int DT, int D, int RT, int NW>
-__global__ __launch_bounds__(NW * 64, (RT == 2 && (NW == 16 || (DT == kBF16 && NW == 8))) ? 4 : 1)
+__global__ __launch_bounds__(NW * 64, (RT == 2 && NW == 8) ? 4 : 1)
 void scores_mfma_kernel(Plan p,
                                                               const typename Elem<DT>::T* __restrict__ q,
                                                               const float* __restrict__ kbar,
@@ -365,6 +365,279 @@ void scores_mfma_kernel(Plan p,
     row_out[J] = row_out[J] * __builtin_amdgcn_exp2f(mJ[J] - M) * inv;
 }
 
+// Ping-pong form for tiles of 513 to 1024 packed rows: 16 waves in two
+// groups of 8 (waves 0-7 hold the first 256 RT rows, waves 8-15 the rest,
+// two waves of each group per SIMD), group 1 one phase behind group 0.  In
+// every phase one group issues the MFMAs of its chunk while the other
+// reduces the chunk it multiplied in the previous phase, so a SIMD's matrix
+// and vector work come from different waves.  (With one 16-wave workgroup
+// per CU and a barrier per chunk, the plain form has every SIMD's four waves
+// in the same phase.  Tiles of up to 512 rows keep the plain form: two of
+// its 8-wave workgroups share a CU and overlap on their own.)
+// Phase p (a barrier after each):
+//   group 0: p = 2c: MFMAs of chunk c; p = 2c + 1: reduce chunk c, then merge
+//            the partials of chunk c - 1 (all 16 waves have written them);
+//   group 1: p = 2c + 1: MFMAs of chunk c, then the global loads of chunk
+//            c + 2; p = 2c + 2: reduce chunk c, then store chunk c + 2 into
+//            the LDS buffer chunk c occupied (group 1 was its last reader).
+// Rows, scores and their accuracy are those of scores_mfma_kernel.
+template <int DT, int D, int RT>
+__global__ __launch_bounds__(1024, 1) void scores_pp_kernel(Plan p,
+                                                            const typename Elem<DT>::T* __restrict__ q,
+                                                            const float* __restrict__ kbar, float c2,
+                                                            float* __restrict__ scores) {
+  if (p.dscale) c2 *= p.dscale[0];  // fp8 q scale kept on the device
+  c2 = __builtin_bit_cast(float, sc_uni(__builtin_bit_cast(int, c2)));  // uniform: a scalar register
+  constexpr int NW = 16;                // waves; groups of GW
+  constexpr int GW = 8;
+  constexpr int GT = GW * 64;           // threads per group
+  constexpr int KS = D / 16;            // k-steps of 16 dims
+  constexpr int LD = D + 8;             // padded LDS row (bf16), 16-byte multiple
+  constexpr int F4 = kChunk * D / 4;    // float4 per kbar chunk
+  constexpr int PF = (F4 + GT - 1) / GT;
+  __shared__ __attribute__((aligned(16))) uint16_t kb[2][2][kChunk * LD];
+  __shared__ float part_m[2][NW][kChunk];
+  __shared__ float part_s[2][NW][kChunk];
+  __shared__ float red_m[kChunk];
+  __shared__ double red_s[kChunk];
+  extern __shared__ float dyn[];  // m_J[nch * 32]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int grp = wave / GW;            // uniform per wave
+  const int gt = tid - grp * GT;        // thread index within the group
+  const int half = lane >> 5;
+  const int jj = lane & 31;
+  const int64_t seg = p.num_segments - 1 - (int64_t)blockIdx.x;  // longest rows first
+  const int b = seq_of_segment(p, seg);
+  const SeqInfo s = p.seq[b];
+  int h, I;
+  segment_tile(s, (int)(seg - s.seg_base), h, I);
+  const int q0 = tile_q0(s, I, p.B);
+  const int R = p.g * tile_nq(s, I, p.B);
+  const int nJ = I + 1;
+  const int nch = (nJ + kChunk - 1) / kChunk;
+  float* mJ = dyn;
+  float* row_out = scores + score_offset(s, h, I);
+  const float* kb_head = kbar + ((int64_t)s.pool_base * p.hkv + h) * D;
+  const int64_t kb_stride = (int64_t)p.hkv * D;  // floats between pooled rows
+
+  // ---- this wave's query rows (A operands), zero beyond R
+  const int row0 = wave * RT * 32;
+  const bool wave_active = row0 < R;
+  sbf16x8_t qa[RT][KS];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int r = row0 + t * 32 + jj;
+    const bool ok = r < R;
+    const int pos = q0 + (ok ? r / p.g : 0);
+    const int hq = h * p.g + (ok ? r % p.g : 0);
+    const int64_t qoff = (q_row(s, pos) * p.hq + hq) * D;
+    if constexpr (DT == kFP8) {
+      uint2 cw[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        cw[ks] = *reinterpret_cast<const uint2*>(q + qoff + ks * 16 + half * 8);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 u = widen_e4m3x8(cw[ks]);
+        if (!ok) u = make_uint4(0, 0, 0, 0);
+        qa[t][ks] = __builtin_bit_cast(sbf16x8_t, u);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (ok) u = *reinterpret_cast<const uint4*>(q + qoff + ks * 16 + half * 8);
+        qa[t][ks] = __builtin_bit_cast(sbf16x8_t, u);
+      }
+    }
+  }
+
+  // ---- kbar chunk staging by one group: raw buffer loads from one scalar
+  // descriptor per chunk (rows past the chunk's last block read zero), then
+  // the two-term split into LDS
+  float4 pf[PF];
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+    const int last = min(kChunk, nJ - c * kChunk) - 1;
+    const float* base = kb_head + (int64_t)c * kChunk * kb_stride;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)sc_uniform_ptr(base), (short)0, sc_uni((last * (int)kb_stride + D) * 4), kScRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int f = gt + i * GT;
+      const uint32_t off = (F4 % GT == 0 || f < F4)
+          ? (uint32_t)(f / (D / 4)) * (uint32_t)kb_stride * 4u + (uint32_t)(f % (D / 4)) * 16u
+          : 0x80000000u;  // past every descriptor: reads zero, never stored
+      pf[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+    }
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int f = gt + i * GT;
+      if (F4 % GT != 0 && f >= F4) break;
+      const int j = f / (D / 4);
+      const int d0 = (f % (D / 4)) * 4;
+      const uint2 p01 = split2_pair(pf[i].x, pf[i].y), p23 = split2_pair(pf[i].z, pf[i].w);
+      const int o = j * LD + d0;
+      *reinterpret_cast<uint2*>(&kb[buf][0][o]) = make_uint2(p01.x, p23.x);
+      *reinterpret_cast<uint2*>(&kb[buf][1][o]) = make_uint2(p01.y, p23.y);
+    }
+  };
+
+  // group 0 stages chunk 0, group 1 chunk 1
+  if (grp == 0 || nch > 1) {
+    fetch(grp);
+    store(grp);
+  }
+  if (tid < kChunk) {
+    red_m[tid] = -INFINITY;
+    red_s[tid] = 0.0;
+  }
+  __syncthreads();
+
+  // merge of chunk cc's partials by group 0: wave gw takes blocks 4 gw ..
+  // 4 gw + 3 of the chunk, a lane the partial of wave sw (of 16) for block
+  // jl, and groups of 16 lanes reduce in a fixed butterfly order.  The lane
+  // group also folds the block into its running pair (rm, rs), kept in LDS
+  // by the group's first lane: the largest block maximum so far and the
+  // float64 sum of S_J 2^(m_J - rm) over its blocks.
+  auto combine = [&](int cc) __attribute__((always_inline)) {
+    const int jl = (tid >> 4) & 31, sw = tid & 15;
+    const float pmv = part_m[cc & 1][sw][jl], psv = part_s[cc & 1][sw][jl];
+    const float m = group_max<16>(pmv);
+    const float S = group_sum<16>(psv * __builtin_amdgcn_exp2f(pmv - (m == -INFINITY ? 0.f : m)));
+    const int J = cc * kChunk + jl;
+    if (J < nJ && sw == 0) {
+      const float rm = red_m[jl];
+      const float nm = fmaxf(rm, m);
+      const float ref = nm == -INFINITY ? 0.f : nm;
+      red_s[jl] = red_s[jl] * (double)__builtin_amdgcn_exp2f(rm - ref) +
+                  (double)S * (double)__builtin_amdgcn_exp2f(m - ref);
+      red_m[jl] = nm;
+      mJ[J] = m;
+      row_out[J] = S;
+    }
+  };
+
+  sf32x16_t acc[RT];
+  auto mfma = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+    }
+    // lo, then hi: the small partial sums first
+#pragma unroll
+    for (int sp = 1; sp >= 0; --sp) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const sbf16x8_t bop = *reinterpret_cast<const sbf16x8_t*>(
+            &kb[c & 1][sp][jj * LD + ks * 16 + half * 8]);
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t][ks], bop, acc[t], 0, 0, 0);
+      }
+    }
+  };
+  // max and sum of exp2(c2 * acc) over the wave's rows of block J; the
+  // maximum is taken on the raw products (c2 > 0) and the scale enters the
+  // exponent's FMA.  Only the chunk past the last block and the row tile
+  // past the last row need masks (a uniform test per wave).
+  auto reduce = [&](int c) __attribute__((always_inline)) {
+    float pm = -INFINITY, ps = 0.f;
+    if (wave_active) {
+      const int J = c * kChunk + jj;
+      float mx = -INFINITY;
+      if (row0 + RT * 32 <= R && (c + 1) * kChunk <= nJ) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[t][i]);
+        }
+      } else {
+        // element i of row tile t is row row0 + 32 t + 8 (i >> 2) + 4 half + (i & 3)
+        int t0 = threadIdx.x;
+        asm volatile("" : "+v"(t0));
+        const int lim = J < nJ ? R - (t0 >> 6) * (RT * 32) - ((t0 >> 5) & 1) * 4 : 0;
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            acc[t][i] = t * 32 + (i >> 2) * 8 + (i & 3) < lim ? acc[t][i] : -INFINITY;
+            mx = fmaxf(mx, acc[t][i]);
+          }
+        }
+      }
+      mx = pair_max(mx);
+      const float nmu = mx == -INFINITY ? 0.f : -mx * c2;
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(fmaf(acc[t][i], c2, nmu));
+      }
+      pm = mx == -INFINITY ? -INFINITY : mx * c2;
+      ps = pair_sum(sum);
+    }
+    if (half == 0) {
+      part_m[c & 1][wave][jj] = pm;
+      part_s[c & 1][wave][jj] = ps;
+    }
+  };
+
+  // Both groups pass 2 nch + 1 barriers; each group's loop keeps a chunk's
+  // accumulators within one iteration.
+  if (grp == 0) {
+    for (int c = 0; c < nch; ++c) {
+      if (wave_active) mfma(c);  // phase 2c
+      __syncthreads();
+      reduce(c);  // phase 2c + 1
+      if (c > 0) combine(c - 1);
+      __syncthreads();
+    }
+    __syncthreads();  // phase 2 nch: group 1 reduces the last chunk
+  } else {
+    __syncthreads();  // phase 0
+    for (int c = 0; c < nch; ++c) {
+      if (wave_active) mfma(c);  // phase 2c + 1
+      if (c + 2 < nch) fetch(c + 2);
+      __syncthreads();
+      reduce(c);  // phase 2c + 2
+      if (c + 2 < nch) store(c & 1);
+      __syncthreads();
+    }
+  }
+  if (grp == 0) combine(nch - 1);
+  __syncthreads();
+  // M_I and the total sum_J S_J 2^(m_J - M_I) from the 32 running pairs
+  // (merged by every thread in the same order), then every score
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kChunk; ++k) M = fmaxf(M, red_m[k]);
+  double tot = 0.0;
+#pragma unroll
+  for (int k = 0; k < kChunk; ++k) {
+    const float mk = red_m[k];
+    if (mk != -INFINITY) tot += red_s[k] * (double)__builtin_amdgcn_exp2f(mk - M);
+  }
+  const float inv = (float)(1.0 / tot);
+  for (int J = tid; J < nJ; J += 1024)
+    row_out[J] = row_out[J] * __builtin_amdgcn_exp2f(mJ[J] - M) * inv;
+}
+
+template <int DT, int D, int RT>
+static hipError_t launch_scores_pp(const Plan& p, const void* q, const float* kbar, float c2,
+                                   float* scores, hipStream_t st) {
+  const int nch = (p.max_nblk + kChunk - 1) / kChunk;
+  const size_t lds = sizeof(float) * nch * kChunk;
+  hipLaunchKernelGGL((scores_pp_kernel<DT, D, RT>), dim3((unsigned)p.num_segments), dim3(1024),
+                     lds, st, p, (const typename Elem<DT>::T*)q, kbar, c2, scores);
+  return hipGetLastError();
+}
+
 template <int DT, int D, int RT, int NW>
 static hipError_t launch_scores_t(const Plan& p, const void* q, const float* kbar, float c2,
                                   float* scores, hipStream_t st) {
@@ -382,7 +655,7 @@ static hipError_t launch_scores_d(const Plan& p, const void* q, const float* kba
   if (rmax <= 128) return launch_scores_t<DT, D, 1, 4>(p, q, kbar, c2, scores, st);
   if (rmax <= 256) return launch_scores_t<DT, D, 2, 4>(p, q, kbar, c2, scores, st);
   if (rmax <= 512) return launch_scores_t<DT, D, 2, 8>(p, q, kbar, c2, scores, st);
-  return launch_scores_t<DT, D, 2, 16>(p, q, kbar, c2, scores, st);
+  return launch_scores_pp<DT, D, 2>(p, q, kbar, c2, scores, st);
 }
 
 bool scores_mfma_supported(const Plan& p, int dtype) {
