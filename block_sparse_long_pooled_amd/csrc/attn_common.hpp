@@ -89,6 +89,20 @@ struct UnitCtx {
   int kend;      // keys >= kend are invisible to every row of the unit
 };
 
+// KV head of the unit at position `local` of a request's one-workgroup-per-
+// unit enumeration (tiles in descending I, then row block, then KV head).
+// The dispatcher deals workgroups to the XCDs round robin, so with the head
+// innermost every XCD would see one head only, and heads differ in how many
+// blocks they select: the XCDs would finish unevenly, and a workgroup waiting
+// for a busy XCD holds back the dispatch of those behind it.  The head
+// therefore turns by one every kHeadTurn groups of hkv units: each XCD keeps a
+// head for 16 consecutive units (their K/V stay warm in its L2) and sees
+// every head over the launch.  Within a group the turn is a permutation.
+constexpr int kHeadTurn = 16;
+__device__ __forceinline__ int unit_head(int64_t local, int hkv) {
+  return (int)((local % hkv + local / ((int64_t)kHeadTurn * hkv)) % hkv);
+}
+
 // KV splits a segment actually uses, at most `splits`: one per 24 steps of
 // estimated work (its selected blocks in 64-key tiles plus an upper bound on
 // its correction chunks), so light segments stay whole and write no partial

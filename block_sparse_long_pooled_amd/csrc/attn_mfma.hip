@@ -10,9 +10,10 @@
 // wave within 256 VGPRs, so two waves share each SIMD).  Packed row r of the tile is
 // position I*B + r / g of query head h*g + r % g, so every staged K/V key
 // serves all g heads of the group.  Units are enumerated heaviest first
-// (longest request first, tiles in descending I) with the KV head innermost,
-// so consecutive workgroups - which the dispatcher spreads over the XCDs
-// round robin - keep one KV head per XCD and its L2.
+// (longest request first, tiles in descending I, then row block) with the KV
+// head innermost, turned every few groups (unit_head) so that the XCDs,
+// which the dispatcher feeds round robin, share the heads evenly while each
+// keeps one head for a run of consecutive units.
 //
 // Pipeline.  The unit's work is a uniform sequence of 64-key steps: the
 // selected blocks from the CSR list walked backwards (B/64 steps each), then
@@ -639,7 +640,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
 
   if constexpr (!PERSIST) {
     // one workgroup per unit, enumerated heaviest first: longest request
-    // first, tiles in descending I, then row block, KV head innermost
+    // first, tiles in descending I, then row block, KV head innermost (turned
+    // every kHeadTurn groups, unit_head)
     const int64_t unit = blockIdx.x;
     int pos = 0;
     while (pos + 1 < p.num_seqs && p.seq[p.order[pos + 1]].unit_base <= unit) ++pos;
@@ -647,7 +649,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const int64_t local = unit - p.seq[b].unit_base;
     const int per_I = p.hkv * units_per_seg;
     const int rem = (int)(local % per_I);
-    run_unit(b, p.seq[b].nblk - 1 - (int)(local / per_I), rem % p.hkv, rem / p.hkv, 0);
+    run_unit(b, p.seq[b].nblk - 1 - (int)(local / per_I), unit_head(local, p.hkv), rem / p.hkv, 0);
   } else {
   // split launch: persistent workgroups take items from the list the
   // preparation kernel wrote (heaviest segments first) until it is empty
