@@ -544,8 +544,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fp8_kernel(
 
   if constexpr (!PERSIST) {
     // one workgroup per unit, enumerated heaviest first: longest request
-    // first, tiles in descending I, then row block, KV head innermost (turned
-    // every kHeadTurn groups, unit_head)
+    // first, tiles in descending I, then row block, KV head innermost.  (The
+    // bf16 kernel turns the head every kHeadTurn groups; here that made no
+    // difference to the time and raised the HBM reads, so each XCD keeps one
+    // head.)
     const int64_t unit = blockIdx.x;
     int pos = 0;
     while (pos + 1 < p.num_seqs && p.seq[p.order[pos + 1]].unit_base <= unit) ++pos;
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fp8_kernel(
     const int64_t local = unit - p.seq[b].unit_base;
     const int per_I = p.hkv * units_per_seg;
     const int rem = (int)(local % per_I);
-    run_unit(b, p.seq[b].nblk - 1 - (int)(local / per_I), unit_head(local, p.hkv), rem / p.hkv, 0);
+    run_unit(b, p.seq[b].nblk - 1 - (int)(local / per_I), rem % p.hkv, rem / p.hkv, 0);
   } else {
     // split launch: persistent workgroups take items from the work list
     const int n_items = queue[1];
