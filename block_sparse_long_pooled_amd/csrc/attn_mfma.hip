@@ -46,6 +46,8 @@
 // the output rescale rare.  Correction terms enter as s*c + log2|B_J| with
 // unselected or invisible columns at -inf.
 #include <algorithm>
+#include <cstddef>
+#include <atomic>
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -440,18 +442,59 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
   }
 }
 
-template <int DT, int D, int NW, int RT, bool PERSIST, bool CORR>
+// The kernel's parameters as one struct, member for member: the layout of the
+// kernel-argument segment (each argument in order at the next offset aligned
+// to its type, as for struct members; checked below against the kernel's
+// signature).  The host packs a launch into it, and persistent unsplit
+// launches read their arguments from the segment through it (opaque_args).
+struct AttnKernArgs {
+  Plan p;
+  KVDesc kv;
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint16_t* kb2;
+  const uint16_t* vb16;
+  const int32_t* cu;
+  const int32_t* idx;
+  float c, out_scale;
+  int correction, dense, units_per_seg, splits;
+  uint16_t* out;
+  float* lse;
+  float* part_o;
+  float* part_ml;
+  const int32_t* items;
+  int* queue;
+};
+
+// The kernel's arguments from the kernel-argument segment through a pointer
+// the compiler cannot follow, so each use is a fresh scalar load: in a
+// persistent workgroup nothing derived from them is hoisted out of the loop
+// over units and kept live through every unit's walk (which left too few
+// registers for the walk's LDS operands to be read ahead: 59 of the 64
+// MFMAs waited on their own operand read, and each step ran 12-15% slower).
+__device__ __forceinline__ const AttnKernArgs* opaque_args() {
+  auto seg = __builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(seg));
+  return (const AttnKernArgs*)(seg);
+}
+
+// PERSIST: workgroups take units from the work list until it is empty.
+// OPQ (persistent unsplit launches): the arguments are read through
+// opaque_args() and units come from per-XCD queues.  Split launches, a few
+// light items per workgroup, keep plain arguments and one shared queue: the
+// OPQ path ran their attention 14% slower.
+template <int DT, int D, int NW, int RT, bool PERSIST, bool CORR, bool OPQ = false>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
-    Plan p, KVDesc kv, const void* __restrict__ q, const void* __restrict__ k,
-    const void* __restrict__ v, const uint16_t* __restrict__ kb2,
-    const uint16_t* __restrict__ vb16, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ idx, float c, float out_scale, int correction, int dense,
-    int units_per_seg, int splits, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ items,
-    int* __restrict__ queue) {
+    Plan p, KVDesc kv_a, const void* __restrict__ q_a, const void* __restrict__ k_a,
+    const void* __restrict__ v_a, const uint16_t* __restrict__ kb2_a,
+    const uint16_t* __restrict__ vb16_a, const int32_t* __restrict__ cu_a,
+    const int32_t* __restrict__ idx_a, float c_a, float out_scale_a, int correction_a,
+    int dense_a, int units_per_seg, int splits_a, uint16_t* __restrict__ out_a,
+    float* __restrict__ lse_a, float* __restrict__ part_o_a, float* __restrict__ part_ml_a,
+    const int32_t* __restrict__ items_a, int* __restrict__ queue_a) {
   using C = AttnCfg<D, NW, RT>;
   static_assert(DT == kBF16, "bf16 inputs only; fp8 takes attn_fp8_kernel");
-  if constexpr (!CORR) correction = 0;  // compiled without correction steps
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKeys * C::KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VLD];
   // correction steps: the lo rows of the pooled keys, a ring of three slots
@@ -466,7 +509,27 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   const int half = lane >> 5;
 
   // One work unit: (segment (b, h, I), row block mt, KV split sp).
+  const Plan& p_outer = p;
   auto run_unit = [&](int b, int I, int h, int mt, int sp) __attribute__((always_inline)) {
+  // the arguments: through the opaque pointer for OPQ, else the parameters
+  const AttnKernArgs* ka = OPQ ? opaque_args() : nullptr;
+  const Plan& p = OPQ ? ka->p : p_outer;
+  const KVDesc& kv = OPQ ? ka->kv : kv_a;
+  const void* q = OPQ ? ka->q : q_a;
+  const void* k = OPQ ? ka->k : k_a;
+  const void* v = OPQ ? ka->v : v_a;
+  const uint16_t* kb2 = OPQ ? ka->kb2 : kb2_a;
+  const uint16_t* vb16 = OPQ ? ka->vb16 : vb16_a;
+  const int32_t* cu = OPQ ? ka->cu : cu_a;
+  const int32_t* idx = OPQ ? ka->idx : idx_a;
+  const float c = OPQ ? ka->c : c_a, out_scale = OPQ ? ka->out_scale : out_scale_a;
+  const int correction = CORR ? (OPQ ? ka->correction : correction_a) : 0;  // compiled without correction steps
+  const int dense = OPQ ? ka->dense : dense_a;
+  const int splits = OPQ ? ka->splits : splits_a;
+  uint16_t* out = OPQ ? ka->out : out_a;
+  float* lse = OPQ ? ka->lse : lse_a;
+  float* part_o = OPQ ? ka->part_o : part_o_a;
+  float* part_ml = OPQ ? ka->part_ml : part_ml_a;
   const SeqInfo s = p.seq[b];
   const int64_t seg = (int64_t)s.seg_base + (int64_t)h * ntile(s) + (I - s.i0);
   const int q0 = tile_q0(s, I, p.B);
@@ -651,16 +714,61 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const int rem = (int)(local % per_I);
     run_unit(b, p.seq[b].nblk - 1 - (int)(local / per_I), unit_head(local, p.hkv), rem / p.hkv, 0);
   } else {
-  // split launch: persistent workgroups take items from the list the
-  // preparation kernel wrote (heaviest segments first) until it is empty
-  const int n_items = queue[1];
+  if constexpr (OPQ) {
+  // unsplit: persistent workgroups take items from the list the preparation
+  // kernel wrote (heaviest first).  Item k belongs to queue k mod 8, the XCD
+  // a one-workgroup-per-item launch would run it on (the dispatcher deals
+  // workgroups to the XCDs round robin); a workgroup drains its own XCD's
+  // queue, then what is left of the others in turn.  Thread 0 keeps the
+  // cursor in LDS and hands each item's code to the workgroup there, and the
+  // decode reads the plan through the opaque pointer, so no value of one unit
+  // stays live into the next.
+  __shared__ int q_cur[2];  // queue being drained, queues found empty
+  if (tid == 0) {
+    q_cur[0] = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7;  // XCC_ID
+    q_cur[1] = 0;
+  }
   for (;;) {
-    if (tid == 0) next_item = atomicAdd(&queue[0], 1);
+    if (tid == 0) {
+      const AttnKernArgs* kq = opaque_args();
+      const int n_items = kq->queue[1];
+      int qx = q_cur[0], tried = q_cur[1], code = -1;
+      while (tried < 8) {
+        const int kk = qx + 8 * atomicAdd(&kq->queue[2 + qx], 1);
+        if (kk < n_items) {
+          code = kq->items[kk];
+          break;
+        }
+        qx = (qx + 1) & 7;
+        ++tried;
+      }
+      q_cur[0] = qx;
+      q_cur[1] = tried;
+      next_item = code;
+    }
+    __syncthreads();
+    const int code = next_item;
+    __syncthreads();  // every wave has read it (and left the last unit's LDS)
+    if (code < 0) break;
+    const Plan& pd = opaque_args()->p;
+    const int64_t seg = code >> 8;
+    int b = 0;
+    while (b + 1 < pd.num_seqs && pd.seq[b + 1].seg_base <= seg) ++b;
+    int h, I;
+    segment_tile(pd.seq[b], (int)(seg - pd.seq[b].seg_base), h, I);
+    run_unit(b, I, h, (code >> 4) & 15, code & 15);
+  }
+  } else {
+  // split launch: persistent workgroups take items from one shared queue
+  // (heaviest segments first) until it is empty
+  const int n_items = queue_a[1];
+  for (;;) {
+    if (tid == 0) next_item = atomicAdd(&queue_a[0], 1);
     __syncthreads();
     const int it = next_item;
     __syncthreads();  // every wave has read it (and left the last unit's LDS)
     if (it >= n_items) break;
-    const int code = items[it];
+    const int code = items_a[it];
     const int64_t seg = code >> 8;
     int b = 0;
     while (b + 1 < p.num_seqs && p.seq[b + 1].seg_base <= seg) ++b;
@@ -669,7 +777,37 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     run_unit(b, I, h, (code >> 4) & 15, code & 15);
   }
   }
+  }
 }
+
+// AttnKernArgs must be laid out as the kernel's parameter list: the offset of
+// every parameter (in order, each at the next offset aligned to its type) is
+// compared with the offset of the struct member of the same rank.
+template <class F>
+struct KernelParams;
+template <class... A>
+struct KernelParams<void(A...)> {
+  static constexpr size_t count = sizeof...(A);
+  static constexpr size_t offset(size_t i) {
+    constexpr size_t size[] = {sizeof(A)...}, align[] = {alignof(A)...};
+    size_t off = 0;
+    for (size_t j = 0;; ++j) {
+      off = (off + align[j] - 1) / align[j] * align[j];
+      if (j == i) return off;
+      off += size[j];
+    }
+  }
+};
+using AttnParams = KernelParams<decltype(attn_mfma_kernel<kBF16, 128, 8, 1, true, true, true>)>;
+static_assert(AttnParams::count == 21, "AttnKernArgs mirrors 21 kernel parameters");
+#define BSLP_ARG_AT(i, m) \
+  static_assert(AttnParams::offset(i) == offsetof(AttnKernArgs, m), "AttnKernArgs." #m);
+BSLP_ARG_AT(0, p) BSLP_ARG_AT(1, kv) BSLP_ARG_AT(2, q) BSLP_ARG_AT(3, k) BSLP_ARG_AT(4, v)
+BSLP_ARG_AT(5, kb2) BSLP_ARG_AT(6, vb16) BSLP_ARG_AT(7, cu) BSLP_ARG_AT(8, idx)
+BSLP_ARG_AT(9, c) BSLP_ARG_AT(10, out_scale) BSLP_ARG_AT(11, correction) BSLP_ARG_AT(12, dense)
+BSLP_ARG_AT(13, units_per_seg) BSLP_ARG_AT(14, splits) BSLP_ARG_AT(15, out) BSLP_ARG_AT(16, lse)
+BSLP_ARG_AT(17, part_o) BSLP_ARG_AT(18, part_ml) BSLP_ARG_AT(19, items) BSLP_ARG_AT(20, queue)
+#undef BSLP_ARG_AT
 
 // Merge of the KV splits of the rows of every split segment: with M =
 // max_u m_u and weights w_u = l_u 2^(m_u - M), O = sum_u w_u O_u / sum_u w_u
@@ -724,14 +862,18 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(Plan p, const int32_t
   }
 }
 
-// Work list of a split launch ("FlashPrefill V2", CSR paragraph, Eq. 18, and
-// the scheduling paragraph after it: splits balanced by selected count,
-// heaviest work first): one workgroup walks the segments in
-// the order of the unsplit launch (longest request first, tiles in
-// descending I, KV head innermost), gives each its split count from its
-// selected count and writes one item (segment << 8 | row block << 4 | split)
-// per (row block, split), with a block-wide prefix sum for the offsets.
-// queue[0] is the next item to take, queue[1] the number of items.
+// Work list of a persistent launch ("FlashPrefill V2", CSR paragraph, Eq. 18,
+// and the scheduling paragraph after it: splits balanced by selected count,
+// heaviest work first): one workgroup walks the segments in the order of the
+// one-workgroup-per-unit launch (longest request first, tiles in descending
+// I, KV head innermost), gives each its split count from its selected count
+// and writes one item (segment << 8 | row block << 4 | split) per (row
+// block, split), with a block-wide prefix sum for the offsets.  Unsplit
+// (splits = 1: every segment has units_per_seg items) the items go in that
+// launch's exact unit order, row block outside the KV head, so item k is the
+// unit it would have run on XCD k mod 8.  queue[0]: next item of one shared
+// queue (split launches); queue[1]: the number of items; queue[2 + x]: next
+// item of XCD x's queue (items x, x + 8, ...; unsplit bf16 launches).
 __global__ __launch_bounds__(1024) void split_items_kernel(Plan p, const int32_t* __restrict__ cu,
                                                            int splits, int correction,
                                                            int units_per_seg,
@@ -773,17 +915,20 @@ __global__ __launch_bounds__(1024) void split_items_kernel(Plan p, const int32_t
     const int off = before + x - n;
     if (n > 0) {
       const int ns = n / units_per_seg;
-      for (int t = 0; t < n; ++t)
-        items[off + t] = (seg << 8) | ((t / ns) << 4) | (t % ns);
+      if (splits == 1) {
+        const int hh = (int)(q % p.hkv);  // q - hh is a multiple of hkv
+        for (int t = 0; t < n; ++t)
+          items[(q - hh) * units_per_seg + t * p.hkv + hh] = (seg << 8) | (t << 4);
+      } else {
+        for (int t = 0; t < n; ++t)
+          items[off + t] = (seg << 8) | ((t / ns) << 4) | (t % ns);
+      }
     }
     __syncthreads();
     if (tid == 1023) carry_s = off + n;
     __syncthreads();
   }
-  if (tid == 0) {
-    queue[0] = 0;
-    queue[1] = carry_s;
-  }
+  if (tid < 10) queue[tid] = tid == 1 ? carry_s : 0;
 }
 
 // float32 pooled means -> bf16 for the correction steps.  Keys become the pair
@@ -850,6 +995,13 @@ size_t attn_pooled_bytes(const Plan& p) {
   return (3 * n * sizeof(uint16_t) + 255) / 256 * 256;
 }
 
+// Unsplit sparse launches with at least this many work units per CU run
+// persistent (64K: 32 per CU, 5% faster than one workgroup per unit; 16K: 8
+// per CU, 4% slower).
+constexpr int64_t kPersistUnitsPerCU = 16;
+// counters after the work list: queue[0 .. 9] (see split_items_kernel) + 2
+constexpr size_t kQueueWords = 12;
+
 size_t attn_split_items(const Plan& p, int splits) {
   const int ups = (p.g * p.B + attn_rows_per_unit(p) - 1) / attn_rows_per_unit(p);
   return (size_t)p.num_segments * ups * splits;
@@ -857,17 +1009,17 @@ size_t attn_split_items(const Plan& p, int splits) {
 
 size_t attn_workspace_bytes(const Plan& p, int splits) {
   size_t bytes = attn_pooled_bytes(p);
-  if (splits > 1)
-    bytes += (size_t)splits * p.total_tokens * p.hq * (p.d + 2) * sizeof(float) +
-             (attn_split_items(p, splits) + 4) * sizeof(int32_t);
-  return bytes;
+  if (splits > 1) bytes += (size_t)splits * p.total_tokens * p.hq * (p.d + 2) * sizeof(float);
+  // the work list and its queue counters (persistent launches)
+  return bytes + (attn_split_items(p, splits) + kQueueWords) * sizeof(int32_t);
 }
 
 SplitBufs split_bufs(const Plan& p, void* workspace, int splits) {
   SplitBufs b;
+  const size_t parts = splits > 1 ? (size_t)splits * p.total_tokens * p.hq : 0;  // partial rows
   b.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + attn_pooled_bytes(p));
-  b.part_ml = b.part_o + (size_t)splits * p.total_tokens * p.hq * p.d;
-  b.items = reinterpret_cast<int32_t*>(b.part_ml + (size_t)splits * p.total_tokens * p.hq * 2);
+  b.part_ml = b.part_o + parts * p.d;
+  b.items = reinterpret_cast<int32_t*>(b.part_ml + parts * 2);
   b.queue = b.items + attn_split_items(p, splits);
   return b;
 }
@@ -879,10 +1031,23 @@ hipError_t launch_split_items(const Plan& pl, const int32_t* cu, int splits, int
   return hipGetLastError();
 }
 
-hipError_t persistent_grid(const Plan& p, int splits, int per_cu, int64_t* grid) {
-  int dev = 0, cus = 0;
+// Compute units of the current device, asked of the runtime once per device
+// (a launch of a few tens of microseconds would otherwise carry the query).
+static hipError_t device_cus(int* cus) {
+  static std::atomic<int> known[64];
+  int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && (*cus = known[dev].load(std::memory_order_relaxed)) > 0)
+    return hipSuccess;
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && dev >= 0 && dev < 64) known[dev].store(*cus, std::memory_order_relaxed);
+  return e;
+}
+
+hipError_t persistent_grid(const Plan& p, int splits, int per_cu, int64_t* grid) {
+  int cus = 0;
+  const hipError_t e = device_cus(&cus);
   if (e != hipSuccess) return e;
   *grid = std::min<int64_t>(attn_split_items(p, splits), (int64_t)cus * std::max(1, per_cu));
   return hipSuccess;
@@ -897,6 +1062,32 @@ hipError_t launch_split_merge(const Plan& p, const int32_t* cu, const SplitBufs&
   else
     hipLaunchKernelGGL((merge_splits_kernel<64>), dim3((unsigned)p.num_segments), dim3(256), 0,
                        st, p, cu, b.part_o, b.part_ml, splits, corr, lse_off, out, lse);
+  return hipGetLastError();
+}
+
+// A persistent launch of `kernel`: as many workgroups as stay resident at
+// once (the occupancy of a compiled kernel does not change, so it is asked
+// once per process), at most one per work item.
+template <void (*kernel)(Plan, KVDesc, const void*, const void*, const void*, const uint16_t*,
+                         const uint16_t*, const int32_t*, const int32_t*, float, float, int, int,
+                         int, int, uint16_t*, float*, float*, float*, const int32_t*, int*)>
+static hipError_t launch_persistent(const Plan& p, int splits, int threads, const AttnKernArgs& ka,
+                                    hipStream_t st) {
+  static std::atomic<int> occupancy{0};
+  int per_cu = occupancy.load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(kernel), threads, 0);
+    if (e != hipSuccess) return e;
+    occupancy.store(per_cu, std::memory_order_relaxed);
+  }
+  int64_t grid = 0;
+  const hipError_t e = persistent_grid(p, splits, per_cu, &grid);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, st, ka.p, ka.kv, ka.q, ka.k,
+                     ka.v, ka.kb2, ka.vb16, ka.cu, ka.idx, ka.c, ka.out_scale, ka.correction,
+                     ka.dense, ka.units_per_seg, ka.splits, ka.out, ka.lse, ka.part_o, ka.part_ml,
+                     ka.items, ka.queue);
   return hipGetLastError();
 }
 
@@ -932,29 +1123,41 @@ static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs&
   const float c = (float)((double)a.lscale * 1.4426950408889634);
   const int splits = a.splits;
   const int corr = a.correction && !a.dense;
-  if (splits == 1) {
-    hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT, false, CORR>), dim3((unsigned)base), dim3(NW * 64), 0,
-                       st, pl, kv, a.q, a.k, a.v, (const uint16_t*)kb2, (const uint16_t*)vb16,
-                       a.cu, a.idx, c, a.v_scale, corr, a.dense, units_per_seg, 1,
-                       (uint16_t*)a.out, a.lse, nullptr, nullptr, nullptr, nullptr);
+  AttnKernArgs ka{pl, kv, a.q, a.k, a.v, kb2, vb16, a.cu, a.idx, c, a.v_scale, corr, a.dense,
+                  units_per_seg, splits, (uint16_t*)a.out, a.lse, nullptr, nullptr, nullptr,
+                  nullptr};
+  // Persistent workgroups over a work list for split launches, and for
+  // unsplit sparse ones with enough units per CU that the queue's cost (a
+  // list-building launch, an atomic per unit) is repaid by the idle time
+  // between one-workgroup-per-unit dispatches it removes; otherwise one
+  // workgroup per unit.
+  int cus = 0;
+  if (splits == 1 && !a.dense && a.workspace && a.cu) {
+    const hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+  }
+  const bool persist =
+      splits > 1 || (cus > 0 && base >= (int64_t)kPersistUnitsPerCU * cus);
+  if (!persist) {
+    hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT, false, CORR>), dim3((unsigned)base),
+                       dim3(NW * 64), 0, st, ka.p, ka.kv, ka.q, ka.k, ka.v, ka.kb2, ka.vb16,
+                       ka.cu, ka.idx, ka.c, ka.out_scale, ka.correction, ka.dense,
+                       ka.units_per_seg, ka.splits, ka.out, ka.lse, ka.part_o, ka.part_ml,
+                       ka.items, ka.queue);
     return hipGetLastError();
   }
   SplitBufs sb = split_bufs(p, a.workspace, splits);
   hipError_t e = launch_split_items(pl, a.cu, splits, corr, units_per_seg, sb, st);
   if (e != hipSuccess) return e;
-  // persistent workgroups: as many as stay resident at once
-  int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, reinterpret_cast<const void*>(&attn_mfma_kernel<DT, D, NW, RT, true, CORR>), NW * 64, 0);
-  if (e != hipSuccess) return e;
-  int64_t grid = 0;
-  e = persistent_grid(p, splits, per_cu, &grid);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, NW, RT, true, CORR>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     st, pl, kv, a.q, a.k, a.v, (const uint16_t*)kb2, (const uint16_t*)vb16,
-                     a.cu, a.idx, c, a.v_scale, corr, a.dense, units_per_seg, splits,
-                     (uint16_t*)a.out, a.lse, sb.part_o, sb.part_ml, sb.items, sb.queue);
-  e = hipGetLastError();
+  ka.part_o = sb.part_o;
+  ka.part_ml = sb.part_ml;
+  ka.items = sb.items;
+  ka.queue = sb.queue;
+  if (splits == 1)
+    return launch_persistent<attn_mfma_kernel<DT, D, NW, RT, true, CORR, true>>(p, splits, NW * 64,
+                                                                                  ka, st);
+  e = launch_persistent<attn_mfma_kernel<DT, D, NW, RT, true, CORR, false>>(p, splits, NW * 64, ka,
+                                                                              st);
   if (e != hipSuccess) return e;
   return launch_split_merge(p, a.cu, sb, splits, corr, 0.f, (uint16_t*)a.out, a.lse, st);
 }

@@ -265,7 +265,10 @@ bslp_status bslp_select_blocks(const bslp_problem* problem, const bslp_select_pa
  * 16-byte aligned, owned by the caller; its contents on entry do not matter
  * and are overwritten (the call keeps bf16 copies of kbar, as hi + lo pairs,
  * and of vbar there; for fp8 the quantised pooled codes; with KV splits the
- * partial results).  A NULL (when bytes are needed), short or misaligned
+ * partial results; and the list of work units, one int32 each, with its
+ * queue counters, which persistent launches take units from: split
+ * launches, and unsplit bf16 ones with at least 16 units per compute unit).
+ * A NULL (when bytes are needed), short or misaligned
  * workspace is BSLP_ERR_WORKSPACE, before any launch.  Calls that overlap in
  * time must not share a workspace. */
 bslp_status bslp_sparse_prefill_attn(const bslp_problem* problem,

@@ -43,8 +43,10 @@ def test_sizes_match_the_layout():
     assert s.pooled_rows == sum(N)
     assert s.num_segments == 2 * sum(N)
     assert s.score_elems == 2 * sum(n * (n + 1) // 2 for n in N)
-    # bf16 copies of the pooled keys and values for the correction steps
-    assert s.workspace_bytes == 3 * s.pooled_rows * 2 * 128 * 2
+    # bf16 copies of the pooled keys and values for the correction steps, then
+    # the work-unit list (an int32 per segment x row block: g*B = 512 rows, 2
+    # row blocks of 256) and its 12 queue words
+    assert s.workspace_bytes == 3 * s.pooled_rows * 2 * 128 * 2 + (s.num_segments * 2 + 12) * 4
 
 
 def _status(fn):
@@ -213,14 +215,15 @@ def test_kv_splits_validated_and_sized():
     assert st == 1
     base = bslp.get_sizes(_problem(kv_splits=1))
     assert base.workspace_bytes == bslp.get_sizes(_problem()).workspace_bytes  # small: no split
+    pooled = 3 * base.pooled_rows * 2 * 128 * 2
+    assert base.workspace_bytes == pooled + (base.num_segments * 2 + 12) * 4
     for u in (2, 5):
         s = bslp.get_sizes(_problem(kv_splits=u))
         # per split: float32 O [T*Hq, d] and (m, l) [T*Hq, 2] after the pooled
         # copies, then the work list (an int32 per segment x row block x split)
-        # and its two counters (+2 spare)
-        items = s.num_segments * 2 * u + 4  # g*B = 512 rows: 2 row blocks of 256
-        assert s.workspace_bytes == (base.workspace_bytes + u * s.total_tokens * 8 * (128 + 2) * 4
-                                     + items * 4)
+        # and its queue words
+        items = s.num_segments * 2 * u + 12  # g*B = 512 rows: 2 row blocks of 256
+        assert s.workspace_bytes == pooled + u * s.total_tokens * 8 * (128 + 2) * 4 + items * 4
     # float32 never splits
     f = bslp.get_sizes(_problem(dtype="f32", kv_splits=4))
     assert f.workspace_bytes == bslp.get_sizes(_problem(dtype="f32", kv_splits=1)).workspace_bytes
@@ -231,7 +234,7 @@ def test_automatic_kv_splits_only_for_small_launches():
     small = bslp.get_sizes(_problem(hq=4, hkv=1, seqlens=[16384]))
     none = bslp.get_sizes(_problem(hq=4, hkv=1, seqlens=[16384], kv_splits=1))
     assert small.workspace_bytes == (none.workspace_bytes + 2 * 16384 * 4 * 130 * 4
-                                     + (small.num_segments * 2 * 2 + 4) * 4)
+                                     + small.num_segments * 2 * (2 - 1) * 4)
     # 64K tokens x 8 KV heads: thousands of units, no split
     big = bslp.get_sizes(_problem(hq=32, hkv=8, seqlens=[65536]))
     assert big.workspace_bytes == bslp.get_sizes(
