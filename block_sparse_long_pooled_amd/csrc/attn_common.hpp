@@ -15,6 +15,8 @@
 //     hold a block of todo = valid & ~selected (valid: J <= I-1).
 #pragma once
 
+#include <cstddef>
+
 #include "common.hpp"
 
 namespace bslp {
@@ -183,6 +185,40 @@ __device__ __forceinline__ Step first_step(const UnitCtx& u, const int32_t* idx,
   advance(st, u, idx, selbits, correction);
   return st;
 }
+
+// A kernel's arguments read from its kernel-argument segment, as the struct
+// Args that mirrors its parameter list, through a pointer the compiler cannot
+// follow, so each use is a fresh scalar load: in a persistent workgroup
+// nothing derived from them is hoisted out of the loop over units and kept
+// live through every unit's walk (which left too few registers for the
+// walk's LDS operands to be read ahead: in the bf16 kernel 59 of the 64
+// MFMAs waited on their own operand read, and each step ran 12-15% slower).
+template <class Args>
+__device__ __forceinline__ const Args* opaque_kernargs() {
+  auto seg = __builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(seg));
+  return (const Args*)(seg);
+}
+
+// KernelParams<decltype(kernel)>::offset(i): where parameter i of a kernel
+// lies in its kernel-argument segment (each parameter in order at the next
+// offset aligned to its type, as struct members are laid out), for checking
+// a struct that mirrors the parameter list member for member.
+template <class F>
+struct KernelParams;
+template <class... A>
+struct KernelParams<void(A...)> {
+  static constexpr size_t count = sizeof...(A);
+  static constexpr size_t offset(size_t i) {
+    constexpr size_t size[] = {sizeof(A)...}, align[] = {alignof(A)...};
+    size_t off = 0;
+    for (size_t j = 0;; ++j) {
+      off = (off + align[j] - 1) / align[j] * align[j];
+      if (j == i) return off;
+      off += size[j];
+    }
+  }
+};
 
 }  // namespace
 

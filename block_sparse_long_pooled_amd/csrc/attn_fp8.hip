@@ -41,6 +41,8 @@
 // V ([Hkv, d, kv tokens], or [pages, Hkv, d, page] when paged) is staged by
 // plain 16-byte copies (the V-layout bullets of the FP8 paragraph).
 #include <algorithm>
+#include <atomic>
+#include <cstddef>
 
 #include "attn_common.hpp"
 #include "launch.hpp"
@@ -380,20 +382,43 @@ __device__ __forceinline__ void f8_step(const uint8_t* Ks, const uint8_t* Vt,
 
 }  // namespace
 
-template <int D, int NW, bool PERSIST, bool CORR, bool VCOL>
+// The kernel's parameters as one struct, member for member (the layout of
+// the kernel-argument segment; checked below against the kernel's
+// signature).  The host packs a launch into it, and persistent unsplit
+// launches read their arguments from the segment through opaque_kernargs.
+struct F8KernArgs {
+  Plan p;
+  KVDesc kv;
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const uint8_t* kq;
+  const uint8_t* vq;
+  const int32_t* cu;
+  const int32_t* idx;
+  float c, out_scale;
+  int correction, dense, units_per_seg, splits;
+  uint16_t* out;
+  float* lse;
+  float* part_o;
+  float* part_ml;
+  const int32_t* items;
+  int* queue;
+};
+
+// PERSIST: workgroups take units from the work list until it is empty.
+// OPQ (persistent unsplit launches): the arguments are read through
+// opaque_kernargs and units come from per-XCD queues; split launches keep
+// plain arguments and one shared queue.
+template <int D, int NW, bool PERSIST, bool CORR, bool VCOL, bool OPQ = false>
 __global__ __launch_bounds__(NW * 64) void attn_fp8_kernel(
-    Plan p, KVDesc kv, const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
-    const uint8_t* __restrict__ v, const uint8_t* __restrict__ kq, const uint8_t* __restrict__ vq,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ idx, float c, float out_scale,
-    int correction, int dense, int units_per_seg, int splits, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml,
-    const int32_t* __restrict__ items, int* __restrict__ queue) {
+    Plan p, KVDesc kv_a, const uint8_t* __restrict__ q_a, const uint8_t* __restrict__ k_a,
+    const uint8_t* __restrict__ v_a, const uint8_t* __restrict__ kq_a, const uint8_t* __restrict__ vq_a,
+    const int32_t* __restrict__ cu_a, const int32_t* __restrict__ idx_a, float c_a, float out_scale_a,
+    int correction_a, int dense_a, int units_per_seg, int splits_a, uint16_t* __restrict__ out_a,
+    float* __restrict__ lse_a, float* __restrict__ part_o_a, float* __restrict__ part_ml_a,
+    const int32_t* __restrict__ items_a, int* __restrict__ queue_a) {
   using C = F8Cfg<D, NW>;
-  if constexpr (!CORR) correction = 0;  // compiled without correction steps
-  if (p.dscale) {  // scales kept on the device
-    c *= p.dscale[0] * p.dscale[1];
-    out_scale = p.dscale[2];
-  }
   __shared__ __attribute__((aligned(16))) uint8_t Ks[2][kKeys * C::KROW];
   __shared__ __attribute__((aligned(16))) uint8_t Vt[2][D * C::VROW];
   __shared__ uint32_t selbits[kMaxBlocksPerSeq / 32];
@@ -404,7 +429,32 @@ __global__ __launch_bounds__(NW * 64) void attn_fp8_kernel(
   const int wave = tid >> 6;
   const int half = lane >> 5;
 
+  const Plan& p_outer = p;
   auto run_unit = [&](int b, int I, int h, int mt, int sp) __attribute__((always_inline)) {
+  // the arguments, from the segment afresh for every unit when OPQ
+  const F8KernArgs* ka = OPQ ? opaque_kernargs<F8KernArgs>() : nullptr;
+  const Plan& p = OPQ ? ka->p : p_outer;
+  const KVDesc& kv = OPQ ? ka->kv : kv_a;
+  const uint8_t* q = OPQ ? ka->q : q_a;
+  const uint8_t* k = OPQ ? ka->k : k_a;
+  const uint8_t* v = OPQ ? ka->v : v_a;
+  const uint8_t* kq = OPQ ? ka->kq : kq_a;
+  const uint8_t* vq = OPQ ? ka->vq : vq_a;
+  const int32_t* cu = OPQ ? ka->cu : cu_a;
+  const int32_t* idx = OPQ ? ka->idx : idx_a;
+  float c = OPQ ? ka->c : c_a, out_scale = OPQ ? ka->out_scale : out_scale_a;
+  if (p.dscale) {  // scales kept on the device
+    c *= p.dscale[0] * p.dscale[1];
+    out_scale = p.dscale[2];
+  }
+  // none when compiled without correction steps
+  const int correction = CORR ? (OPQ ? ka->correction : correction_a) : 0;
+  const int dense = OPQ ? ka->dense : dense_a;
+  const int splits = OPQ ? ka->splits : splits_a;
+  uint16_t* out = OPQ ? ka->out : out_a;
+  float* lse = OPQ ? ka->lse : lse_a;
+  float* part_o = OPQ ? ka->part_o : part_o_a;
+  float* part_ml = OPQ ? ka->part_ml : part_ml_a;
   const SeqInfo s = p.seq[b];
   const int64_t seg = (int64_t)s.seg_base + (int64_t)h * ntile(s) + (I - s.i0);
   const int q0 = tile_q0(s, I, p.B);
@@ -556,16 +606,54 @@ __global__ __launch_bounds__(NW * 64) void attn_fp8_kernel(
     const int per_I = p.hkv * units_per_seg;
     const int rem = (int)(local % per_I);
     run_unit(b, p.seq[b].nblk - 1 - (int)(local / per_I), rem % p.hkv, rem / p.hkv, 0);
+  } else if constexpr (OPQ) {
+    // unsplit: item k in queue k mod 8 (the XCD a one-workgroup-per-unit
+    // launch would run it on); the own XCD's queue first, then the others
+    __shared__ int q_cur[2];  // queue being drained, queues found empty
+    if (tid == 0) {
+      q_cur[0] = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7;  // XCC_ID
+      q_cur[1] = 0;
+    }
+    for (;;) {
+      if (tid == 0) {
+        const F8KernArgs* kg = opaque_kernargs<F8KernArgs>();
+        const int n_items = kg->queue[1];
+        int qx = q_cur[0], tried = q_cur[1], code = -1;
+        while (tried < 8) {
+          const int kk = qx + 8 * atomicAdd(&kg->queue[2 + qx], 1);
+          if (kk < n_items) {
+            code = kg->items[kk];
+            break;
+          }
+          qx = (qx + 1) & 7;
+          ++tried;
+        }
+        q_cur[0] = qx;
+        q_cur[1] = tried;
+        next_item = code;
+      }
+      __syncthreads();
+      const int code = next_item;
+      __syncthreads();  // every wave has read it (and left the last unit's LDS)
+      if (code < 0) break;
+      const Plan& pd = opaque_kernargs<F8KernArgs>()->p;
+      const int64_t seg = code >> 8;
+      int b = 0;
+      while (b + 1 < pd.num_seqs && pd.seq[b + 1].seg_base <= seg) ++b;
+      int h, I;
+      segment_tile(pd.seq[b], (int)(seg - pd.seq[b].seg_base), h, I);
+      run_unit(b, I, h, (code >> 4) & 15, code & 15);
+    }
   } else {
     // split launch: persistent workgroups take items from the work list
-    const int n_items = queue[1];
+    const int n_items = queue_a[1];
     for (;;) {
-      if (tid == 0) next_item = atomicAdd(&queue[0], 1);
+      if (tid == 0) next_item = atomicAdd(&queue_a[0], 1);
       __syncthreads();
       const int it = next_item;
       __syncthreads();  // every wave has read it (and left the last unit's LDS)
       if (it >= n_items) break;
-      const int code = items[it];
+      const int code = items_a[it];
       const int64_t seg = code >> 8;
       int b = 0;
       while (b + 1 < p.num_seqs && p.seq[b + 1].seg_base <= seg) ++b;
@@ -741,6 +829,44 @@ hipError_t launch_pool_v_dmajor(const Plan& p, const KVDesc& kv, const void* v, 
 
 namespace {
 
+// F8KernArgs must be laid out as the kernel's parameter list.
+using F8Params = KernelParams<decltype(attn_fp8_kernel<128, 8, true, true, false, true>)>;
+static_assert(F8Params::count == 21, "F8KernArgs mirrors 21 kernel parameters");
+#define BSLP_ARG_AT(i, m) \
+  static_assert(F8Params::offset(i) == offsetof(F8KernArgs, m), "F8KernArgs." #m);
+BSLP_ARG_AT(0, p) BSLP_ARG_AT(1, kv) BSLP_ARG_AT(2, q) BSLP_ARG_AT(3, k) BSLP_ARG_AT(4, v)
+BSLP_ARG_AT(5, kq) BSLP_ARG_AT(6, vq) BSLP_ARG_AT(7, cu) BSLP_ARG_AT(8, idx)
+BSLP_ARG_AT(9, c) BSLP_ARG_AT(10, out_scale) BSLP_ARG_AT(11, correction) BSLP_ARG_AT(12, dense)
+BSLP_ARG_AT(13, units_per_seg) BSLP_ARG_AT(14, splits) BSLP_ARG_AT(15, out) BSLP_ARG_AT(16, lse)
+BSLP_ARG_AT(17, part_o) BSLP_ARG_AT(18, part_ml) BSLP_ARG_AT(19, items) BSLP_ARG_AT(20, queue)
+#undef BSLP_ARG_AT
+
+// A persistent launch of `kernel`: as many workgroups as stay resident at
+// once (asked once per process and instantiation), at most one per item.
+template <void (*kernel)(Plan, KVDesc, const uint8_t*, const uint8_t*, const uint8_t*,
+                         const uint8_t*, const uint8_t*, const int32_t*, const int32_t*, float,
+                         float, int, int, int, int, uint16_t*, float*, float*, float*,
+                         const int32_t*, int*)>
+hipError_t launch_persistent_f8(const Plan& p, int splits, int threads, const F8KernArgs& ka,
+                                hipStream_t st) {
+  static std::atomic<int> occupancy{0};
+  int per_cu = occupancy.load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(kernel), threads, 0);
+    if (e != hipSuccess) return e;
+    occupancy.store(per_cu, std::memory_order_relaxed);
+  }
+  int64_t grid = 0;
+  const hipError_t e = persistent_grid(p, splits, per_cu, &grid);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, st, ka.p, ka.kv, ka.q, ka.k,
+                     ka.v, ka.kq, ka.vq, ka.cu, ka.idx, ka.c, ka.out_scale, ka.correction,
+                     ka.dense, ka.units_per_seg, ka.splits, ka.out, ka.lse, ka.part_o, ka.part_ml,
+                     ka.items, ka.queue);
+  return hipGetLastError();
+}
+
 template <int D, int NW, bool CORR, bool VCOL>
 hipError_t launch_fp8_t(const Plan& p, const KVDesc& kv, const AttnArgs& a, hipStream_t st) {
   const int rows = F8Cfg<D, NW>::ROWS;
@@ -771,32 +897,36 @@ hipError_t launch_fp8_t(const Plan& p, const KVDesc& kv, const AttnArgs& a, hipS
   // logits of the codes: softmax_scale * q_scale * k_scale, in units of log2
   const float c = (float)((double)a.lscale * (double)a.k_scale * 1.4426950408889634);
   const int splits = a.splits;
-  const auto* qq = static_cast<const uint8_t*>(a.q);
-  const auto* kk = static_cast<const uint8_t*>(a.k);
-  const auto* vv = static_cast<const uint8_t*>(a.v);
-  if (splits == 1) {
+  F8KernArgs ka{pl, kv, static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
+                static_cast<const uint8_t*>(a.v), kq, vq, a.cu, a.idx, c, a.v_scale, corr,
+                a.dense, units_per_seg, splits, (uint16_t*)a.out, a.lse, nullptr, nullptr,
+                nullptr, nullptr};
+  // persistent workgroups as for bf16: split launches, and unsplit sparse
+  // ones with enough units per CU; otherwise one workgroup per unit
+  int cus = 0;
+  if (splits == 1 && !a.dense && a.workspace && a.cu) {
+    const hipError_t e = attn_device_cus(&cus);
+    if (e != hipSuccess) return e;
+  }
+  if (!(splits > 1 || (cus > 0 && base >= kPersistUnitsPerCU * cus))) {
     hipLaunchKernelGGL((attn_fp8_kernel<D, NW, false, CORR, VCOL>), dim3((unsigned)base),
-                       dim3(NW * 64), 0, st, pl, kv, qq, kk, vv, (const uint8_t*)kq,
-                       (const uint8_t*)vq, a.cu, a.idx, c, a.v_scale, corr, a.dense,
-                       units_per_seg, 1, (uint16_t*)a.out, a.lse, nullptr, nullptr, nullptr,
-                       nullptr);
+                       dim3(NW * 64), 0, st, ka.p, ka.kv, ka.q, ka.k, ka.v, ka.kq, ka.vq, ka.cu,
+                       ka.idx, ka.c, ka.out_scale, ka.correction, ka.dense, ka.units_per_seg,
+                       ka.splits, ka.out, ka.lse, ka.part_o, ka.part_ml, ka.items, ka.queue);
     return hipGetLastError();
   }
   SplitBufs sb = split_bufs(p, a.workspace, splits);
   hipError_t e = launch_split_items(pl, a.cu, splits, corr, units_per_seg, sb, st);
   if (e != hipSuccess) return e;
-  int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, reinterpret_cast<const void*>(&attn_fp8_kernel<D, NW, true, CORR, VCOL>), NW * 64, 0);
-  if (e != hipSuccess) return e;
-  int64_t grid = 0;
-  e = persistent_grid(p, splits, per_cu, &grid);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_fp8_kernel<D, NW, true, CORR, VCOL>), dim3((unsigned)grid),
-                     dim3(NW * 64), 0, st, pl, kv, qq, kk, vv, (const uint8_t*)kq,
-                     (const uint8_t*)vq, a.cu, a.idx, c, a.v_scale, corr, a.dense, units_per_seg,
-                     splits, (uint16_t*)a.out, a.lse, sb.part_o, sb.part_ml, sb.items, sb.queue);
-  e = hipGetLastError();
+  ka.part_o = sb.part_o;
+  ka.part_ml = sb.part_ml;
+  ka.items = sb.items;
+  ka.queue = sb.queue;
+  if (splits == 1)
+    return launch_persistent_f8<attn_fp8_kernel<D, NW, true, CORR, VCOL, true>>(p, splits, NW * 64,
+                                                                               ka, st);
+  e = launch_persistent_f8<attn_fp8_kernel<D, NW, true, CORR, VCOL, false>>(p, splits, NW * 64, ka,
+                                                                            st);
   if (e != hipSuccess) return e;
   return launch_split_merge(p, a.cu, sb, splits, corr, 8.f * kLn2, (uint16_t*)a.out, a.lse, st);
 }

@@ -467,16 +467,8 @@ struct AttnKernArgs {
   int* queue;
 };
 
-// The kernel's arguments from the kernel-argument segment through a pointer
-// the compiler cannot follow, so each use is a fresh scalar load: in a
-// persistent workgroup nothing derived from them is hoisted out of the loop
-// over units and kept live through every unit's walk (which left too few
-// registers for the walk's LDS operands to be read ahead: 59 of the 64
-// MFMAs waited on their own operand read, and each step ran 12-15% slower).
 __device__ __forceinline__ const AttnKernArgs* opaque_args() {
-  auto seg = __builtin_amdgcn_kernarg_segment_ptr();
-  asm volatile("" : "+s"(seg));
-  return (const AttnKernArgs*)(seg);
+  return opaque_kernargs<AttnKernArgs>();
 }
 
 // PERSIST: workgroups take units from the work list until it is empty.
@@ -780,24 +772,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   }
 }
 
-// AttnKernArgs must be laid out as the kernel's parameter list: the offset of
-// every parameter (in order, each at the next offset aligned to its type) is
-// compared with the offset of the struct member of the same rank.
-template <class F>
-struct KernelParams;
-template <class... A>
-struct KernelParams<void(A...)> {
-  static constexpr size_t count = sizeof...(A);
-  static constexpr size_t offset(size_t i) {
-    constexpr size_t size[] = {sizeof(A)...}, align[] = {alignof(A)...};
-    size_t off = 0;
-    for (size_t j = 0;; ++j) {
-      off = (off + align[j] - 1) / align[j] * align[j];
-      if (j == i) return off;
-      off += size[j];
-    }
-  }
-};
+// AttnKernArgs must be laid out as the kernel's parameter list.
 using AttnParams = KernelParams<decltype(attn_mfma_kernel<kBF16, 128, 8, 1, true, true, true>)>;
 static_assert(AttnParams::count == 21, "AttnKernArgs mirrors 21 kernel parameters");
 #define BSLP_ARG_AT(i, m) \
@@ -995,10 +970,6 @@ size_t attn_pooled_bytes(const Plan& p) {
   return (3 * n * sizeof(uint16_t) + 255) / 256 * 256;
 }
 
-// Unsplit sparse launches with at least this many work units per CU run
-// persistent (64K: 32 per CU, 5% faster than one workgroup per unit; 16K: 8
-// per CU, 4% slower).
-constexpr int64_t kPersistUnitsPerCU = 16;
 // counters after the work list: queue[0 .. 9] (see split_items_kernel) + 2
 constexpr size_t kQueueWords = 12;
 
@@ -1031,9 +1002,9 @@ hipError_t launch_split_items(const Plan& pl, const int32_t* cu, int splits, int
   return hipGetLastError();
 }
 
-// Compute units of the current device, asked of the runtime once per device
-// (a launch of a few tens of microseconds would otherwise carry the query).
-static hipError_t device_cus(int* cus) {
+// Asked once per device: a launch of a few tens of microseconds would
+// otherwise carry the query.
+hipError_t attn_device_cus(int* cus) {
   static std::atomic<int> known[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1047,7 +1018,7 @@ static hipError_t device_cus(int* cus) {
 
 hipError_t persistent_grid(const Plan& p, int splits, int per_cu, int64_t* grid) {
   int cus = 0;
-  const hipError_t e = device_cus(&cus);
+  const hipError_t e = attn_device_cus(&cus);
   if (e != hipSuccess) return e;
   *grid = std::min<int64_t>(attn_split_items(p, splits), (int64_t)cus * std::max(1, per_cu));
   return hipSuccess;
@@ -1133,7 +1104,7 @@ static hipError_t launch_mfma_t(const Plan& p, const KVDesc& kv, const AttnArgs&
   // workgroup per unit.
   int cus = 0;
   if (splits == 1 && !a.dense && a.workspace && a.cu) {
-    const hipError_t e = device_cus(&cus);
+    const hipError_t e = attn_device_cus(&cus);
     if (e != hipSuccess) return e;
   }
   const bool persist =

@@ -80,6 +80,13 @@ hipError_t launch_split_items(const Plan& pl, const int32_t* cu, int splits, int
 hipError_t launch_split_merge(const Plan& p, const int32_t* cu, const SplitBufs& b, int splits,
                               int corr, float lse_off, uint16_t* out, float* lse, hipStream_t st);
 hipError_t persistent_grid(const Plan& p, int splits, int per_cu, int64_t* grid);
+// Compute units of the current device (asked of the runtime once per device).
+hipError_t attn_device_cus(int* cus);
+// Unsplit sparse launches with at least this many work units per CU run
+// persistent over per-XCD queues (bf16 64K: 32 per CU, 5% faster than one
+// workgroup per unit; 16K: 8 per CU, 4% slower; fp8 128K: 32 per CU, 3%
+// faster).
+constexpr int64_t kPersistUnitsPerCU = 16;
 
 // fp8 inputs on the fp8 matrix cores (e4m3 probabilities, FlashPrefill V2 FP8
 // arithmetic); with p.v_dmajor, V is [Hkv, d, kv tokens] (contiguous) or
