@@ -902,9 +902,12 @@ hipError_t launch_fp8_t(const Plan& p, const KVDesc& kv, const AttnArgs& a, hipS
                 a.dense, units_per_seg, splits, (uint16_t*)a.out, a.lse, nullptr, nullptr,
                 nullptr, nullptr};
   // persistent workgroups as for bf16: split launches, and unsplit sparse
-  // ones with enough units per CU; otherwise one workgroup per unit
+  // ones with enough units per CU; otherwise one workgroup per unit.  With
+  // d-major V the unsplit launch stays one workgroup per unit: at 128K the
+  // queue made its attention 4.6% slower (4.53 -> 4.74 ms) where it made the
+  // row-major one 3.3% faster (4.34 -> 4.20 ms).
   int cus = 0;
-  if (splits == 1 && !a.dense && a.workspace && a.cu) {
+  if (!VCOL && splits == 1 && !a.dense && a.workspace && a.cu) {
     const hipError_t e = attn_device_cus(&cus);
     if (e != hipSuccess) return e;
   }
@@ -922,9 +925,11 @@ hipError_t launch_fp8_t(const Plan& p, const KVDesc& kv, const AttnArgs& a, hipS
   ka.part_ml = sb.part_ml;
   ka.items = sb.items;
   ka.queue = sb.queue;
-  if (splits == 1)
-    return launch_persistent_f8<attn_fp8_kernel<D, NW, true, CORR, VCOL, true>>(p, splits, NW * 64,
-                                                                               ka, st);
+  if constexpr (!VCOL) {
+    if (splits == 1)
+      return launch_persistent_f8<attn_fp8_kernel<D, NW, true, CORR, VCOL, true>>(p, splits,
+                                                                                 NW * 64, ka, st);
+  }
   e = launch_persistent_f8<attn_fp8_kernel<D, NW, true, CORR, VCOL, false>>(p, splits, NW * 64, ka,
                                                                             st);
   if (e != hipSuccess) return e;
