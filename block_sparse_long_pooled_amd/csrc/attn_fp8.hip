@@ -123,7 +123,8 @@ __device__ __forceinline__ void f8_fetch(F8Prefetch<D, NW>& pf, const Step& st, 
     for (int i = 0; i < C::KL; ++i) {
       const int f = min(tid + i * C::NT, C::NK - 1);
       const int key = f / (D / 8), piece = f % (D / 8);
-      const auto w = __builtin_amdgcn_raw_buffer_load_b64(rk, (int)(key * stride + piece * 8), 0, 0);
+      const auto w =
+          __builtin_amdgcn_raw_buffer_load_b64(rk, (int)(key * stride + piece * 8), 0, 0);
       pf.k[i] = make_uint2(w[0], w[1]);
     }
     if (VCOL && exact) {
@@ -374,7 +375,8 @@ __device__ __forceinline__ void f8_step(const uint8_t* Ks, const uint8_t* Vt,
   for (int dt = 0; dt < C::DT; ++dt) {
     const int d = 32 * dt + rl;
     const uint8_t* row = Vt + d * C::VROW;
-    oacc[dt] = mfma8(load32(row + (((2 * half) ^ vswz(d)) << 4), row + (((2 * half + 1) ^ vswz(d)) << 4)),
+    oacc[dt] = mfma8(load32(row + (((2 * half) ^ vswz(d)) << 4),
+                            row + (((2 * half + 1) ^ vswz(d)) << 4)),
                      pb, oacc[dt]);
   }
   lacc = mfma8(ones, pb, lacc);
@@ -413,9 +415,10 @@ struct F8KernArgs {
 template <int D, int NW, bool PERSIST, bool CORR, bool VCOL, bool OPQ = false>
 __global__ __launch_bounds__(NW * 64) void attn_fp8_kernel(
     Plan p, KVDesc kv_a, const uint8_t* __restrict__ q_a, const uint8_t* __restrict__ k_a,
-    const uint8_t* __restrict__ v_a, const uint8_t* __restrict__ kq_a, const uint8_t* __restrict__ vq_a,
-    const int32_t* __restrict__ cu_a, const int32_t* __restrict__ idx_a, float c_a, float out_scale_a,
-    int correction_a, int dense_a, int units_per_seg, int splits_a, uint16_t* __restrict__ out_a,
+    const uint8_t* __restrict__ v_a, const uint8_t* __restrict__ kq_a,
+    const uint8_t* __restrict__ vq_a, const int32_t* __restrict__ cu_a,
+    const int32_t* __restrict__ idx_a, float c_a, float out_scale_a, int correction_a,
+    int dense_a, int units_per_seg, int splits_a, uint16_t* __restrict__ out_a,
     float* __restrict__ lse_a, float* __restrict__ part_o_a, float* __restrict__ part_ml_a,
     const int32_t* __restrict__ items_a, int* __restrict__ queue_a) {
   using C = F8Cfg<D, NW>;
@@ -953,8 +956,10 @@ hipError_t launch_fp8_d(const Plan& p, const KVDesc& kv, const AttnArgs& a, hipS
 
 hipError_t launch_attn_fp8(const Plan& p, const KVDesc& kv, const AttnArgs& a, hipStream_t st) {
   if (p.v_dmajor)
-    return p.d == 128 ? launch_fp8_d<128, true>(p, kv, a, st) : launch_fp8_d<64, true>(p, kv, a, st);
-  return p.d == 128 ? launch_fp8_d<128, false>(p, kv, a, st) : launch_fp8_d<64, false>(p, kv, a, st);
+    return p.d == 128 ? launch_fp8_d<128, true>(p, kv, a, st)
+                      : launch_fp8_d<64, true>(p, kv, a, st);
+  return p.d == 128 ? launch_fp8_d<128, false>(p, kv, a, st)
+                    : launch_fp8_d<64, false>(p, kv, a, st);
 }
 
 }  // namespace bslp

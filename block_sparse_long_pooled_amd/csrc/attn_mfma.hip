@@ -248,7 +248,8 @@ __device__ __forceinline__ void fetch_step(Prefetch<D, NW, RT>& pf,
 #pragma unroll
   for (int i = 0; i < C::KL; ++i) kkey[i] = min(min(tid + i * C::NT, C::KUN - 1) / C::KU, last);
 #pragma unroll
-  for (int i = 0; i < C::VL; ++i) vkey[i] = min(2 * (min(tid + i * C::NT, C::VPN - 1) % PAIRS), last);
+  for (int i = 0; i < C::VL; ++i)
+    vkey[i] = min(2 * (min(tid + i * C::NT, C::VPN - 1) % PAIRS), last);
   int64_t krow[C::KL], vrow0[C::VL], vrow1[C::VL];
 #pragma unroll
   for (int i = 0; i < C::KL; ++i) krow[i] = kv.row(u.b, u.kv_start, key0 + kkey[i]);
@@ -515,7 +516,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   const int32_t* cu = OPQ ? ka->cu : cu_a;
   const int32_t* idx = OPQ ? ka->idx : idx_a;
   const float c = OPQ ? ka->c : c_a, out_scale = OPQ ? ka->out_scale : out_scale_a;
-  const int correction = CORR ? (OPQ ? ka->correction : correction_a) : 0;  // compiled without correction steps
+  // none when compiled without correction steps
+  const int correction = CORR ? (OPQ ? ka->correction : correction_a) : 0;
   const int dense = OPQ ? ka->dense : dense_a;
   const int splits = OPQ ? ka->splits : splits_a;
   uint16_t* out = OPQ ? ka->out : out_a;
@@ -639,8 +641,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
         mode = kCorrMode;
         todo = chunk_todo(selbits, cur.c, I);
       }
-      compute_step<D, NW, RT, CORR>(Ks[buf], Kl[ls], Vt[buf], qf, oacc, m_run, l_run, c, mode, key0, s.len,
-                              qpos, todo, bias);
+      compute_step<D, NW, RT, CORR>(Ks[buf], Kl[ls], Vt[buf], qf, oacc, m_run, l_run, c, mode,
+                                    key0, s.len, qpos, todo, bias);
     }
     cur = nxt;
     nxt = nn;
@@ -833,7 +835,8 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(Plan p, const int32_t
     *reinterpret_cast<uint2*>(out + row * D + d) =
         make_uint2(pack_bf16x2(o0 * inv, o1 * inv), pack_bf16x2(o2 * inv, o3 * inv));
     if (lse && d == 0)
-      lse[(int64_t)hq * p.total_tokens + tok] = L > 0.f ? M * kLn2 + __logf(L) - lse_off : -INFINITY;
+      lse[(int64_t)hq * p.total_tokens + tok] =
+          L > 0.f ? M * kLn2 + __logf(L) - lse_off : -INFINITY;
   }
 }
 
@@ -1150,7 +1153,8 @@ static hipError_t launch_mfma_d(const Plan& p, const KVDesc& kv, const AttnArgs&
 hipError_t launch_attn_mfma(const Plan& p, const KVDesc& kv, int dtype, const AttnArgs& a,
                             hipStream_t st) {
   if (dtype != kBF16) return hipErrorInvalidValue;  // fp8 runs in attn_fp8.hip
-  return p.d == 128 ? launch_mfma_d<kBF16, 128>(p, kv, a, st) : launch_mfma_d<kBF16, 64>(p, kv, a, st);
+  return p.d == 128 ? launch_mfma_d<kBF16, 128>(p, kv, a, st)
+                    : launch_mfma_d<kBF16, 64>(p, kv, a, st);
 }
 
 }  // namespace bslp
