@@ -290,7 +290,9 @@ __device__ __forceinline__ f32x16_t mfma8(const i32x8_t& a, const i32x8_t& b, co
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-enum F8Mode : int { kF8Plain = 0, kF8Diag = 1, kF8Corr = 2 };
+// kF8CorrAll: a correction chunk of 64 valid pooled blocks, none selected
+// (nothing to mask)
+enum F8Mode : int { kF8Plain = 0, kF8Diag = 1, kF8Corr = 2, kF8CorrAll = 3 };
 
 // One 64-key step of one wave: S^T = K Q^T on the bf16 matrix cores (codes
 // widened exactly, so the logits carry only float32 rounding), exact running
@@ -317,7 +319,7 @@ __device__ __forceinline__ void f8_step(const uint8_t* Ks, const uint8_t* Vt,
     }
   }
   // the lane's value e of tile kt is key key0 + 32 half + 16 kt + e
-  if (mode != kF8Plain) {
+  if (mode == kF8Diag || mode == kF8Corr) {
     uint32_t bits;
     int lim;
     if (mode == kF8Diag) {
@@ -337,7 +339,7 @@ __device__ __forceinline__ void f8_step(const uint8_t* Ks, const uint8_t* Vt,
       }
     }
   }
-  const float cb = mode == kF8Corr ? bias : 0.f;
+  const float cb = mode >= kF8Corr ? bias : 0.f;
   float mx = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
@@ -546,9 +548,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fp8_kernel(
         key0 = cur.J * p.B + cur.hf * kKeys;
         mode = cur.J == I ? kF8Diag : kF8Plain;
       } else {
-        mode = kF8Corr;
         key0 = kCorrRows * cur.c;
         todo = chunk_todo(selbits, cur.c, I);
+        mode = todo == ~0ull ? kF8CorrAll : kF8Corr;
       }
       f8_step<D, NW>(Ks[buf], Vt[buf], qf, oacc, lacc, m_run, c, mode, key0, qpos, todo, bias);
     }
