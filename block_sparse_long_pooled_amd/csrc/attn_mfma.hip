@@ -306,7 +306,9 @@ __device__ __forceinline__ void store_step(const Prefetch<D, NW, RT>& pf, uint16
   }
 }
 
-enum Mode : int { kPlain = 0, kDiag = 1, kCorrMode = 2 };
+// kCorrAll: a correction chunk of 64 valid pooled blocks, none selected
+// (nothing to mask)
+enum Mode : int { kPlain = 0, kDiag = 1, kCorrMode = 2, kCorrAll = 3 };
 
 // One 64-key step of one wave over its RT row tiles: S^T = K Q^T, online
 // softmax, O^T += V^T P^T.  `mode` is uniform across the workgroup.
@@ -345,7 +347,7 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
   // small terms), then the hi rows', into the same accumulators.  The lo rows
   // are [16-byte dim chunk][key]: the operand of key kt*32 + key_l, dims
   // 16 ks + 8 half .. +7, is chunk 2 ks + half.
-  if (CORR && mode == kCorrMode) {
+  if (CORR && mode >= kCorrMode) {
     const char* lb = reinterpret_cast<const char*>(Kl) + half * C::KCS + key_l * 16;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
@@ -365,7 +367,7 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
   }
   // masks: diagonal block (token causality and the request end) or the
   // correction chunk's todo bits; branch-free per element, uniform per step
-  if (mode != kPlain) {
+  if (mode == kDiag || mode == kCorrMode) {
     uint64_t bits;
     if (mode == kDiag) {
       const int nvis = len - key0;  // >= 1
@@ -392,7 +394,7 @@ __device__ __forceinline__ void compute_step(const uint16_t* Ks, const uint16_t*
   // The running maximum is raised only when the step's maximum exceeds it by
   // more than 8, so probabilities stay below 2^8 and the output rescale is
   // rare; the final normalisation uses the same reference, so it is exact.
-  const float cb = mode == kCorrMode ? bias : 0.f;
+  const float cb = mode >= kCorrMode ? bias : 0.f;
   bf16x8_t pb[RT][4];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -638,8 +640,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
         key0 = cur.J * p.B + cur.hf * kKeys;
         mode = cur.J == I ? kDiag : kPlain;
       } else {
-        mode = kCorrMode;
         todo = chunk_todo(selbits, cur.c, I);
+        mode = todo == ~0ull ? kCorrAll : kCorrMode;
       }
       compute_step<D, NW, RT, CORR>(Ks[buf], Kl[ls], Vt[buf], qf, oacc, m_run, l_run, c, mode,
                                     key0, s.len, qpos, todo, bias);
