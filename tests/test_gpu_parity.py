@@ -87,6 +87,35 @@ def test_small_shapes(w):
     _full(w, 3)
 
 
+# ----------------------------------------------------------------- chunks with nothing to mask
+
+# No sink block and a high threshold: tiles past block 64 leave whole
+# correction chunks of 64 pooled blocks with none selected, which the
+# kernels run without the masking pass ("FlashPrefill V2", Sec. 3.2 / Fig. 3
+# paragraph: the todo set is every valid block not selected).
+UNSELECTED_CHUNKS = [
+    Workload("corr-unselected-bf16", (8200,), 4, 1, 64, 64, "bf16", sink=0, window=1,
+             recent=0, alpha=0.5),
+    Workload("corr-unselected-fp8", (8200,), 8, 1, 64, 64, "fp8", sigma_c=1.5, sink=0,
+             window=1, recent=0, alpha=0.5),
+]
+
+
+@pytest.mark.parametrize("w", UNSELECTED_CHUNKS, ids=lambda w: w.name)
+def test_correction_chunks_with_nothing_to_mask(w):
+    _, g, _ = _full(w, 3)
+    # (tile, chunk) pairs whose chunk holds 64 valid blocks (J <= I - 1), none
+    # selected: the case must occur for the test to cover it
+    full_unselected = 0
+    for (_, _, I, s, _) in segments(w.seqlens, w.hkv, w.block):
+        sel = np.zeros(I + 1, dtype=bool)
+        sel[g.idx[g.cu[s]:g.cu[s + 1]]] = True
+        for c in range(I // 64):
+            full_unselected += not sel[64 * c:64 * c + 64].any()
+    log(f"[parity] {w.name}: {full_unselected} full correction chunks with no selected block")
+    assert full_unselected > 0
+
+
 @pytest.mark.parametrize("correction", [True, False])
 def test_alpha_zero_is_dense(correction):
     w = Workload("dense-bf16", (700,), 8, 2, 128, 64, "bf16", alpha=0.0, sink=0, window=0,
